@@ -1,0 +1,264 @@
+"""Throughput of the MI355X ring-attention forward on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+one simulated device's share of an 8-way ZigZag causal ring at its real shape
+(total sequence 131072 in 16 chunks of 8192, the device's query shard =
+chunks {2, 13}, 8 heads, d = 128, bf16, N(0,1)), run as the ring runs it:
+8 step-kernel launches over the 8 key/value shards in ring order, each
+followed (after the first) by a log-sum-exp merge into the running output.
+
+`value` is causal-adjusted TFLOP/s: 4*d FLOP per visible (query, key) pair
+per query head (2d for QK^T, 2d for PV; exponentials and masked work are not
+counted), pairs counted from the positions alone.  Timing uses HIP events on
+the stream the kernels run on; inputs are resident in HBM before timing.
+
+Also reported: the roofline entry of the dominant kernel (the step kernel,
+MFMA bound, against the 2.5 PFLOP/s dense bf16 peak), the fp64 CPU oracle
+timed on a bounded sample of the same workload, and other workloads timed
+the same way (extras).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="query rows of the workload the CPU oracle times")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- pair counts
+
+def causal_pairs(q_pos, k_pos):
+    """Visible (query, key) pairs: keys with position <= the query's."""
+    k_sorted = np.sort(np.asarray(k_pos))
+    return int(np.searchsorted(k_sorted, np.asarray(q_pos), side="right").sum())
+
+
+def runs_positions(runs):
+    return np.concatenate([np.arange(a, a + n) for a, n in runs]) if runs else np.zeros(0, int)
+
+
+# ---------------------------------------------------------------- timing
+
+class Timer:
+    """Accumulates HIP-event durations of launches on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __call__(self, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        self.pairs.append((a, b))
+        return r
+
+    def total_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+
+def step_plan(N, W, rank, c):
+    """The launches of one ZigZag ring device (as ring.ring_forward_steps runs
+    them): per step the query runs, key runs and whether it is merged."""
+    from ring_attention_amd import ring
+    plan = []
+    q_runs = ring.shard_rows(N, W, True, rank)
+    for s in range(W):
+        src = (rank - s) % W
+        k_runs = ring.shard_rows(N, W, True, src)
+        if s == 0:
+            plan.append((q_runs, k_runs))
+        elif s <= rank:
+            plan.append((q_runs, k_runs[:1]))
+        else:
+            plan.append((q_runs[1:], k_runs))
+    return plan
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see DESIGN.md on sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ring_attention_amd import binding, ring, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    w = workloads.workload(4)
+    W, rank, N, d, Hq = w.W, w.rank, w.N, w.d, w.Hq
+    c = N // (2 * W)
+    q, k, v = workloads.make_inputs(w, device=dev)
+    ks = [ring.shard(k, W, True, r) for r in range(W)]
+    vs = [ring.shard(v, W, True, r) for r in range(W)]
+    torch.cuda.synchronize()
+
+    plan = step_plan(N, W, rank, c)
+    step_pairs = [causal_pairs(runs_positions(qr), runs_positions(kr)) for qr, kr in plan]
+    pairs = sum(step_pairs)
+    flop_per_step = 4 * d * Hq * w.B * pairs
+
+    def one_step(timer=None):
+        return ring.ring_forward_steps(q, ks, vs, W, True, rank, causal=True)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        one_step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    value = flop_per_step / (ms_per_step * 1e-3) / 1e12
+
+    # per-launch timing of the dominant kernel (the step kernel), on the same stream
+    kern = Timer(torch)
+    merge_t = Timer(torch)
+    orig_step, orig_merge = binding.fwd_step, binding.merge
+    try:
+        ring.binding.fwd_step = lambda *a, **kw: kern(lambda: orig_step(*a, **kw))
+        ring.binding.merge = lambda *a, **kw: merge_t(lambda: orig_merge(*a, **kw))
+        for _ in range(args.steps):
+            one_step()
+    finally:
+        ring.binding.fwd_step, ring.binding.merge = orig_step, orig_merge
+    n_launch = len(kern.pairs)
+    kern_ms = kern.total_ms() / n_launch
+    merge_ms = merge_t.total_ms() / max(1, len(merge_t.pairs))
+    flop_per_launch = 4 * d * Hq * w.B * pairs / len(plan)
+    achieved = flop_per_launch / (kern_ms * 1e-3) / 1e12
+
+    # fused single launch of the same share
+    fo = fl = None
+    for _ in range(args.warmup):
+        fo, fl = binding.fwd(q, k, v, causal=True, n_ring_steps=W, zigzag=True, rank=rank)
+    ft = Timer(torch)
+    for _ in range(args.steps):
+        ft(lambda: binding.fwd(q, k, v, causal=True, n_ring_steps=W, zigzag=True, rank=rank))
+    fused_ms = ft.total_ms() / args.steps
+    fused_value = flop_per_step / (fused_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: N(0,1) bf16 q/k/v from a seeded torch generator, resident in HBM",
+        "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "N": N, "Hq": Hq, "Hkv": w.Hkv,
+                   "d": d, "causal": True, "ring": W, "zigzag": True, "rank": rank,
+                   "mode": "8 ring-step launches + 7 LSE merges",
+                   "visible_pairs_per_head": pairs},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "fwd_mfma_kernel<Bf16,128,out_f32>",
+                     "avg_launch_ms": round(kern_ms, 4), "launches": n_launch},
+        "merge_avg_ms": round(merge_ms, 4),
+        "fused": {"value": round(fused_value, 2), "ms": round(fused_ms, 4),
+                  "pct_of_peak": round(100 * fused_value / PEAK_BF16_TFLOPS, 2)},
+    }
+    del fo, fl
+
+    if not args.no_extras:
+        extras = {}
+        for idx in (2, 3, 5):
+            we = workloads.workload(idx)
+            qe, ke, ve = workloads.make_inputs(we, device=dev)
+            if we.causal:
+                qpos = np.arange(we.Nq)
+                pe = causal_pairs(qpos, np.arange(we.N))
+            else:
+                pe = we.Nq * we.N
+            fe = 4 * we.d * we.Hq * we.B * pe
+            reps = 3 if idx == 5 else args.steps
+            for _ in range(1 if idx == 5 else args.warmup):
+                binding.fwd(qe, ke, ve, causal=we.causal, n_ring_steps=we.W, zigzag=we.zigzag,
+                            rank=we.rank)
+            te = Timer(torch)
+            for _ in range(reps):
+                te(lambda: binding.fwd(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
+                                       zigzag=we.zigzag, rank=we.rank))
+            ms = te.total_ms() / reps
+            extras[we.name] = {"ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
+                               "pct_of_peak": round(100 * fe / (ms * 1e-3) / 1e12
+                                                    / PEAK_BF16_TFLOPS, 2)}
+            del qe, ke, ve
+            torch.cuda.empty_cache()
+        result["extras"] = extras
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, q, k, v, n_rows):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from oracle import layouts
+
+    rows = np.stack([np.zeros(n_rows, np.int64),
+                     np.random.default_rng(7).choice(w.Nq, n_rows, replace=False),
+                     np.random.default_rng(8).integers(0, w.Hq, n_rows)], axis=1)
+    qpos = layouts.zigzag_shard_positions(w.N, w.W, w.rank)
+    qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+    threads = oracle.default_threads()
+    t = time.perf_counter()
+    oracle.attention(qh, kh, vh, causal=True, q_pos=qpos, rows=rows, n_threads=threads)
+    dt = time.perf_counter() - t
+    pairs = int((qpos[rows[:, 1]] + 1).sum())  # keys 0..N-1, natural order
+    flop = 4 * w.d * pairs
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_rows} seeded (row, head) query rows of the same workload, "
+                      f"{pairs} visible pairs, {dt:.2f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+/*
+ * rattn.h -- C ABI of the MI355X (gfx950) exact ring-attention forward.
+ *
+ * The operation is exact attention, softmax(scale * Q K^T) V (guijiagi.com
+ * "ring-attention-explained", memory-wall section, first formula), computed
+ * blockwise with an online softmax: every query tile keeps a running row
+ * maximum m, a running sum l and an unnormalised accumulator O while it
+ * streams over key/value tiles, and divides by l once at the end (yz520gzy
+ * FlashAttention chapter, FlashAttention-2 deferred normalisation).  Results
+ * of separate key sets (ring steps) are combined with a log-sum-exp
+ * correction (Twinkle "Sequence parallel and Ring Attention", forward-pass
+ * section, update_out_and_lse).
+ *
+ * Conventions shared by every entry point
+ *   - Layout (batch, sequence, heads, head_dim), contiguous, as in the
+ *     flash-attn usage example of the yz520gzy chapter:
+ *       q [B, Nq, Hq, d]     k, v [B, Nk, Hkv, d]     out [B, Nq, Hq, d]
+ *       lse [B, Nq, Hq] float32, natural logarithm of sum_j exp(scale*s_j)
+ *   - GQA: query head h reads key/value head h / (Hq / Hkv).
+ *   - Causal: a key is visible to a query iff its global position is not
+ *     after the query's (youngju.dev "Ring Attention" analysis, causal step).
+ *   - scale <= 0 (or NaN) selects 1/sqrt(d).
+ *   - d must be one of 16, 32, 64, 128.
+ *   - Every pointer argument that names a tensor is a DEVICE pointer owned by
+ *     the caller; it may be NULL only when that tensor has no rows.  The library allocates no memory, keeps no global state and
+ *     never synchronises the host: work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and completes asynchronously.
+ *     Inputs must stay valid until the stream has passed the call.
+ *   - Host-side argument checks run before anything is enqueued; a failed
+ *     check returns a negative status and enqueues nothing.  RATTN_EHIP
+ *     reports a HIP launch error (hipGetLastError after the launch).
+ *   - Rows with no visible key get out = 0 and lse = -inf.
+ *   - out/lse must not overlap q, k or v.
+ */
+#ifndef RATTN_H
+#define RATTN_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define RATTN_API __attribute__((visibility("default")))
+#else
+#define RATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RATTN_OK = 0,
+  RATTN_EINVAL = -1,       /* invalid argument (null pointer, bad size, ...) */
+  RATTN_EUNSUPPORTED = -2, /* valid but not implemented (d, dtype, W > 32) */
+  RATTN_EHIP = -3          /* HIP reported an error when enqueueing */
+} rattn_status;
+
+typedef enum { RATTN_F32 = 0, RATTN_F16 = 1, RATTN_BF16 = 2 } rattn_dtype;
+
+/*
+ * Whole ring schedule in one call.
+ *
+ * k, v hold all N key/value rows in natural order (row index == position).
+ * n_ring_steps = W >= 1 simulated devices (at most 32).  zigzag = 0: device r
+ * holds contiguous block r of N/W rows (ultralytics.com "Ring Attention", how
+ * it works); zigzag = 1: device r holds chunks r and 2W-1-r of the 2W chunks
+ * of N/(2W) rows (Twinkle page, ZigZag section).  Each simulated device visits
+ * the key/value blocks in ring order, block (r - s) mod W at step s.
+ *   rank = -1 : q holds all N rows in natural order (Nq == N) and the
+ *               schedules of all W devices run in one launch.
+ *   rank = r  : q holds device r's shard (Nq == N/W): block r, or for ZigZag
+ *               [chunk r ; chunk 2W-1-r].
+ * N must be a multiple of W (of 2W with zigzag).  out has q's dtype.
+ * Without causal masking the result does not depend on W, zigzag or rank.
+ */
+RATTN_API int rattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+              int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d, int dtype,
+              float scale, int causal, int n_ring_steps, int zigzag, int rank,
+              void* stream);
+
+/*
+ * One ring step: the attention of a set of query rows over one received
+ * key/value shard (the per-step block call of the Twinkle forward pass).
+ *
+ * Query rows [0, q_seg_len[0]) sit at positions q_seg_start[0] + i and rows
+ * [q_seg_len[0], Nq) at q_seg_start[1] + (i - q_seg_len[0]); likewise for the
+ * Nk key/value rows with k_seg_*.  q_seg_len[0] + q_seg_len[1] == Nq and
+ * k_seg_len[0] + k_seg_len[1] == Nk (a length may be 0).  The four segment
+ * arrays are HOST pointers to two int64 each.
+ * Writes the normalised float32 partial out_part [B, Nq, Hq, d] and
+ * lse_part [B, Nq, Hq]; rows that see no key get 0 and -inf, which the merge
+ * treats as an empty partial.
+ */
+RATTN_API int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk,
+                   float* out_part, float* lse_part, int B, int Hq, int Hkv,
+                   int64_t Nq, int64_t Nk, int d, int dtype, float scale, int causal,
+                   const int64_t* q_seg_start, const int64_t* q_seg_len,
+                   const int64_t* k_seg_start, const int64_t* k_seg_len, void* stream);
+
+/*
+ * In-place log-sum-exp merge (Twinkle page, update_out_and_lse; computed as
+ * lse' = logaddexp(lse, blk_lse), out' = e^(lse-lse') out + e^(blk_lse-lse') blk_out):
+ *   (out, lse)[b, row_off + i, h] <- (out, lse)[b, row_off + i, h]
+ *                                    (+) (blk_out, blk_lse)[b, i, h]
+ * for i in [0, Nb).  out [B, Nq, H, d] float32, lse [B, Nq, H] float32,
+ * blk_out [B, Nb, H, d] float32, blk_lse [B, Nb, H] float32.
+ * A side with lse = -inf is empty and leaves the other unchanged; two empty
+ * sides give out = 0, lse = -inf.  Requires row_off + Nb <= Nq; the block
+ * buffers must not overlap out/lse.  All tensor pointers 16-byte aligned.
+ */
+RATTN_API int rattn_merge(float* out, float* lse, const float* blk_out, const float* blk_lse,
+                int B, int H, int64_t Nq, int64_t Nb, int64_t row_off, int d,
+                void* stream);
+
+/* Static description of a status code; never NULL. */
+RATTN_API const char* rattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RATTN_H */

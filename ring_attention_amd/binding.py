@@ -1,0 +1,177 @@
+"""ctypes binding of librattn.so -- argument marshalling only.
+
+Every function here checks tensor metadata, allocates outputs with torch on
+the inputs' device, and calls the C entry point of the same name on the
+current torch stream.  All arithmetic runs in the HIP kernels; there is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librattn.so")
+
+RATTN_OK, RATTN_EINVAL, RATTN_EUNSUPPORTED, RATTN_EHIP = 0, -1, -2, -3
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+# Exported symbols, in the order include/rattn.h declares them.
+EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_merge", "rattn_status_string")
+
+
+class RattnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load librattn.so (built by ring_attention_amd.build) and declare signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(
+            f"{p} is missing: build it with `python -m ring_attention_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(p)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.rattn_fwd.restype = i32
+    lib.rattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
+                              i32, i32, i32, i32, vp]
+    lib.rattn_fwd_step.restype = i32
+    lib.rattn_fwd_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
+                                   i32, i64p, i64p, i64p, i64p, vp]
+    lib.rattn_merge.restype = i32
+    lib.rattn_merge.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp]
+    lib.rattn_status_string.restype = ctypes.c_char_p
+    lib.rattn_status_string.argtypes = [i32]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().rattn_status_string(int(status)).decode()
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != RATTN_OK:
+        raise RattnError(fn, rc)
+
+
+def _qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor [B, N, H, d]")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODES:
+        raise ValueError("q, k, v must share one dtype among float32/float16/bfloat16")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("shape mismatch between q and k/v")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def _scale(scale):
+    return 0.0 if scale is None else float(scale)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        n_ring_steps: int = 1, zigzag: bool = False, rank: int = -1,
+        scale: float | None = None, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None):
+    """Whole simulated ring schedule in one launch (rattn_fwd).
+
+    q [B, Nq, Hq, d], k/v [B, N, Hkv, d] natural order.  rank=-1: q holds all N
+    rows; rank=r: q holds device r's shard.  Returns (out [B,Nq,Hq,d] in q's
+    dtype, lse [B,Nq,Hq] float32).
+    """
+    _qkv(q, k, v)
+    B, Nq, Hq, d = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    rc = lib.rattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       B, Hq, Hkv, Nq, N, d, DTYPE_CODES[q.dtype], _scale(scale),
+                       int(bool(causal)), int(n_ring_steps), int(bool(zigzag)), int(rank),
+                       _stream(q))
+    _check("rattn_fwd", rc)
+    return out, lse
+
+
+def fwd_step(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, causal: bool,
+             q_segs, k_segs, scale: float | None = None,
+             out_part: torch.Tensor | None = None, lse_part: torch.Tensor | None = None):
+    """One ring step (rattn_fwd_step): normalised float32 partial and its lse.
+
+    q_segs / k_segs: up to two (start_position, length) pairs covering the rows
+    of q / k_blk in order.
+    """
+    _qkv(q, k_blk, v_blk)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k_blk.shape[1], k_blk.shape[2]
+
+    def segs(pairs):
+        pairs = list(pairs) + [(0, 0)] * (2 - len(pairs))
+        if len(pairs) != 2:
+            raise ValueError("at most two segments")
+        starts = (ctypes.c_int64 * 2)(*[int(p[0]) for p in pairs])
+        lens = (ctypes.c_int64 * 2)(*[int(p[1]) for p in pairs])
+        return starts, lens
+
+    qs, ql = segs(q_segs)
+    kst, kl = segs(k_segs)
+    if out_part is None:
+        out_part = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    rc = lib.rattn_fwd_step(q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+                            out_part.data_ptr(), lse_part.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                            DTYPE_CODES[q.dtype], _scale(scale), int(bool(causal)),
+                            qs, ql, kst, kl, _stream(q))
+    _check("rattn_fwd_step", rc)
+    return out_part, lse_part
+
+
+def merge(out: torch.Tensor, lse: torch.Tensor, blk_out: torch.Tensor, blk_lse: torch.Tensor,
+          row_off: int = 0):
+    """In-place log-sum-exp merge (rattn_merge) of a float32 partial into (out, lse)."""
+    for name, t in (("out", out), ("lse", lse), ("blk_out", blk_out), ("blk_lse", blk_lse)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if out.dim() != 4 or blk_out.dim() != 4:
+        raise ValueError("out and blk_out must be [B, N, H, d]")
+    B, Nq, H, d = out.shape
+    Nb = blk_out.shape[1]
+    if blk_out.shape != (B, Nb, H, d) or lse.shape != (B, Nq, H) or blk_lse.shape != (B, Nb, H):
+        raise ValueError("merge: shape mismatch")
+    lib = load_library()
+    rc = lib.rattn_merge(out.data_ptr(), lse.data_ptr(), blk_out.data_ptr(), blk_lse.data_ptr(),
+                         B, H, Nq, Nb, int(row_off), d, _stream(out))
+    _check("rattn_merge", rc)
+    return out, lse
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

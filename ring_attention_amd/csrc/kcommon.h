@@ -1,0 +1,112 @@
+// kcommon.h -- device-side helpers shared by the forward kernels (HIP path only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ring_sched.h"
+
+namespace rattn {
+
+// Launch parameters common to the forward kernels.
+struct FwdParams {
+  int32_t B, Hq, Hkv;
+  int32_t group;     // Hq / Hkv
+  int64_t Nq;        // query rows in q (per batch)
+  int64_t Nk;        // key/value rows in k, v (per batch)
+  float c;           // scale * log2(e): scores are exponentiated with exp2
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// 16-bit storage types and their MFMA operand vectors.
+struct Bf16 {
+  typedef __bf16 elem;
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+struct F16 {
+  typedef _Float16 elem;
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+struct F32 {
+  typedef float elem;
+};
+
+// Round-to-nearest-even conversion to the storage type (v_cvt_pk_bf16_f32 /
+// v_cvt_f16_f32 on gfx950).
+template <typename TT>
+__device__ __forceinline__ typename TT::elem to_elem(float x) {
+  return (typename TT::elem)x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Number of leading keys of a key tile visible to one query: keys kk < limit
+// are visible.  `rows` keys are present in the tile; under the causal rule
+// key kk (at position kpos0 + kk) is visible iff kk <= qpos - kpos0 = rel.
+__device__ __forceinline__ int visible_limit(int rows, int32_t causal, int64_t rel) {
+  if (!causal) return rows;
+  const int64_t n = rel + 1;
+  return n <= 0 ? 0 : (n < rows ? (int)n : rows);
+}
+
+// XCD-aware placement of (batch, head) pairs: consecutive workgroups are
+// dealt round-robin to the 8 XCDs, so workgroups b, b+8, b+16, ... share an
+// XCD and its L2.  Remap so that those get adjacent heads (with GQA, the query
+// heads of one key/value head), which then hit the same K/V lines in L2.
+__device__ __forceinline__ int32_t xcd_head_swizzle(int32_t bh, int32_t BH) {
+  return (BH & 7) == 0 ? (bh & 7) * (BH >> 3) + (bh >> 3) : bh;
+}
+
+// Cursor over the live key tiles of one query tile, in ring order.
+struct TileCursor {
+  int32_t v;   // visit index
+  int32_t nv;  // number of visits
+  int64_t t;   // tile within the visit
+  int64_t nt;  // live tiles in the visit
+  Run run;
+};
+
+template <int BC>
+__device__ __forceinline__ void cursor_settle(TileCursor& c, const Sched& s, int32_t rank,
+                                              int64_t qhi) {
+  while (c.t >= c.nt) {
+    ++c.v;
+    if (c.v >= c.nv) return;
+    c.run = visit(s, rank, c.v);
+    c.nt = live_tiles(c.run, qhi, s.causal, BC);
+    c.t = 0;
+  }
+}
+
+template <int BC>
+__device__ __forceinline__ TileCursor cursor_begin(const Sched& s, int32_t rank, int64_t qhi) {
+  TileCursor c;
+  c.nv = num_visits(s);
+  c.v = -1;
+  c.t = 0;
+  c.nt = 0;
+  c.run.row0 = c.run.len = c.run.pos0 = 0;
+  cursor_settle<BC>(c, s, rank, qhi);
+  return c;
+}
+
+template <int BC>
+__device__ __forceinline__ void cursor_next(TileCursor& c, const Sched& s, int32_t rank,
+                                            int64_t qhi) {
+  ++c.t;
+  cursor_settle<BC>(c, s, rank, qhi);
+}
+
+}  // namespace rattn

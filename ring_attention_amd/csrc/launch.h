@@ -1,0 +1,26 @@
+// launch.h -- host-side entry points of the kernels (HIP path only).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "kcommon.h"
+
+namespace rattn {
+
+// Query rows per tile of each forward kernel; the schedule is built for it.
+constexpr int kGenericBr = 64;
+constexpr int kMfmaBr = 128;
+
+hipError_t launch_fwd_generic(int dtype, int d, const void* q, const void* k, const void* v,
+                              void* out, float* lse, bool out_f32, const FwdParams& p,
+                              const Sched& s, hipStream_t stream);
+
+// 16-bit inputs, d in {32, 64, 128}.
+hipError_t launch_fwd_mfma(int dtype, int d, const void* q, const void* k, const void* v,
+                           void* out, float* lse, bool out_f32, const FwdParams& p,
+                           const Sched& s, hipStream_t stream);
+
+hipError_t launch_merge(float* out, float* lse, const float* blk_out, const float* blk_lse,
+                        int B, int H, int64_t Nq, int64_t Nb, int64_t row_off, int d,
+                        hipStream_t stream);
+
+}  // namespace rattn

@@ -1,0 +1,225 @@
+// rattn_abi.hip -- the C ABI (include/rattn.h): argument checks, the ring
+// scheduler that turns (W, zigzag, rank) or explicit segments into query
+// segments and key/value visits, and kernel dispatch.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "launch.h"
+#include "rattn.h"
+#include "ring_sched.h"
+
+namespace rattn {
+namespace {
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+// a*b without signed overflow, for sizes that are all >= 0.
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+// Element count of a [B, N, H, d] tensor fits comfortably in 64-bit offsets.
+bool tensor_ok(int64_t B, int64_t N, int64_t H, int64_t d) {
+  int64_t x;
+  return mul_ok(B, N, &x) && mul_ok(x, H, &x) && mul_ok(x, d, &x) && x < ((int64_t)1 << 60);
+}
+
+// Fill tile_begin in longest-first order (causal: the segment with the latest
+// positions first, and inside a segment the last tile first) and count tiles.
+int finalize(Sched& s, QSeg* segs, int n, int br) {
+  int m = 0;
+  for (int i = 0; i < n; ++i)
+    if (segs[i].len > 0) segs[m++] = segs[i];
+  if (s.causal)
+    std::stable_sort(segs, segs + m, [](const QSeg& a, const QSeg& b) {
+      return a.pos0 + a.len > b.pos0 + b.len;
+    });
+  int64_t tiles = 0;
+  for (int i = 0; i < m; ++i) {
+    segs[i].tile_begin = (int32_t)tiles;
+    tiles += (segs[i].len + br - 1) / br;
+    if (tiles > INT32_MAX) return RATTN_EUNSUPPORTED;
+    s.qseg[i] = segs[i];
+  }
+  s.n_qseg = m;
+  s.n_tiles = (int32_t)tiles;
+  s.reverse = s.causal ? 1 : 0;
+  s.br = br;
+  return RATTN_OK;
+}
+
+int check_dtype_d(int dtype, int d) {
+  if (dtype < RATTN_F32 || dtype > RATTN_BF16) return RATTN_EINVAL;
+  if (!supported_d(d)) return RATTN_EUNSUPPORTED;
+  return RATTN_OK;
+}
+
+bool use_mfma(int dtype, int d) { return dtype != RATTN_F32 && d >= 32; }
+
+float resolve_scale(float scale, int d) {
+  return (scale > 0.f && isfinite(scale)) ? scale : (float)(1.0 / sqrt((double)d));
+}
+
+FwdParams make_params(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, float scale) {
+  FwdParams p;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  return p;
+}
+
+int dispatch(int dtype, int d, const void* q, const void* k, const void* v, void* out,
+             float* lse, bool out_f32, const FwdParams& p, const Sched& s, int64_t grid,
+             void* stream) {
+  if (grid > INT32_MAX) return RATTN_EUNSUPPORTED;
+  hipError_t e;
+  if (use_mfma(dtype, d))
+    e = launch_fwd_mfma(dtype, d, q, k, v, out, lse, out_f32, p, s, (hipStream_t)stream);
+  else
+    e = launch_fwd_generic(dtype, d, q, k, v, out, lse, out_f32, p, s, (hipStream_t)stream);
+  return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+}
+
+}  // namespace
+}  // namespace rattn
+
+using namespace rattn;
+
+extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d, int dtype,
+                         float scale, int causal, int n_ring_steps, int zigzag, int rank,
+                         void* stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
+  if (N < 0 || Nq < 0) return RATTN_EINVAL;
+  // a pointer may be null only when its tensor is empty
+  if ((Nq > 0 && (!q || !out || !lse)) || (N > 0 && (!k || !v))) return RATTN_EINVAL;
+  int rc = check_dtype_d(dtype, d);
+  if (rc != RATTN_OK) return rc;
+  if ((causal != 0 && causal != 1) || (zigzag != 0 && zigzag != 1)) return RATTN_EINVAL;
+  if (n_ring_steps < 1) return RATTN_EINVAL;
+  if (n_ring_steps > kMaxQSeg / 2) return RATTN_EUNSUPPORTED;
+  const int W = n_ring_steps;
+  const int64_t parts = zigzag ? 2 * (int64_t)W : W;
+  if (N % parts != 0) return RATTN_EINVAL;
+  if (rank < -1 || rank >= W) return RATTN_EINVAL;
+  if (rank == -1 ? Nq != N : Nq != N / W) return RATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4))
+    return RATTN_EINVAL;
+  if (!tensor_ok(B, N, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
+  if (Nq == 0) return RATTN_OK;
+
+  const int br = use_mfma(dtype, d) ? kMfmaBr : kGenericBr;
+  Sched s;
+  memset(&s, 0, sizeof s);
+  s.W = W;
+  s.causal = causal;
+  QSeg segs[kMaxQSeg];
+  memset(segs, 0, sizeof segs);
+  int n = 0;
+  if (!zigzag) {
+    s.mode = kVisitContiguousRing;
+    s.blk = N / W;
+    if (rank >= 0) {
+      segs[n++] = QSeg{0, Nq, rank * s.blk, rank, 0};
+    } else {
+      for (int g = 0; g < W; ++g) segs[n++] = QSeg{g * s.blk, s.blk, g * s.blk, g, 0};
+    }
+  } else {
+    s.mode = kVisitZigZagRing;
+    const int64_t c = N / (2 * (int64_t)W);
+    s.blk = c;
+    if (rank >= 0) {
+      segs[n++] = QSeg{0, c, rank * c, rank, 0};
+      segs[n++] = QSeg{c, c, (2 * (int64_t)W - 1 - rank) * c, rank, 0};
+    } else {
+      for (int g = 0; g < 2 * W; ++g)
+        segs[n++] = QSeg{g * c, c, g * c, g < W ? g : 2 * W - 1 - g, 0};
+    }
+  }
+  rc = finalize(s, segs, n, br);
+  if (rc != RATTN_OK) return rc;
+  const FwdParams p = make_params(B, Hq, Hkv, Nq, N, resolve_scale(scale, d));
+  return dispatch(dtype, d, q, k, v, out, lse, false, p, s, (int64_t)s.n_tiles * B * Hq, stream);
+}
+
+extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk,
+                              float* out_part, float* lse_part, int B, int Hq, int Hkv,
+                              int64_t Nq, int64_t Nk, int d, int dtype, float scale, int causal,
+                              const int64_t* q_seg_start, const int64_t* q_seg_len,
+                              const int64_t* k_seg_start, const int64_t* k_seg_len,
+                              void* stream) {
+  if (!q_seg_start || !q_seg_len || !k_seg_start || !k_seg_len) return RATTN_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
+  if (Nq < 0 || Nk < 0) return RATTN_EINVAL;
+  // a pointer may be null only when its tensor is empty
+  if ((Nq > 0 && (!q || !out_part || !lse_part)) || (Nk > 0 && (!k_blk || !v_blk)))
+    return RATTN_EINVAL;
+  int rc = check_dtype_d(dtype, d);
+  if (rc != RATTN_OK) return rc;
+  if (causal != 0 && causal != 1) return RATTN_EINVAL;
+  for (int i = 0; i < 2; ++i)
+    if (q_seg_len[i] < 0 || k_seg_len[i] < 0) return RATTN_EINVAL;
+  if (q_seg_len[0] + q_seg_len[1] != Nq || k_seg_len[0] + k_seg_len[1] != Nk)
+    return RATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) ||
+      !aligned(out_part, 16) || !aligned(lse_part, 4))
+    return RATTN_EINVAL;
+  if (!tensor_ok(B, Nq > Nk ? Nq : Nk, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
+  if (Nq == 0) return RATTN_OK;
+
+  const int br = use_mfma(dtype, d) ? kMfmaBr : kGenericBr;
+  Sched s;
+  memset(&s, 0, sizeof s);
+  s.mode = kVisitExplicit;
+  s.W = 1;
+  s.causal = causal;
+  s.n_kruns = 0;
+  if (k_seg_len[0] > 0) s.kruns[s.n_kruns++] = Run{0, k_seg_len[0], k_seg_start[0]};
+  if (k_seg_len[1] > 0) s.kruns[s.n_kruns++] = Run{k_seg_len[0], k_seg_len[1], k_seg_start[1]};
+  QSeg segs[2] = {QSeg{0, q_seg_len[0], q_seg_start[0], 0, 0},
+                  QSeg{q_seg_len[0], q_seg_len[1], q_seg_start[1], 0, 0}};
+  rc = finalize(s, segs, 2, br);
+  if (rc != RATTN_OK) return rc;
+  const FwdParams p = make_params(B, Hq, Hkv, Nq, Nk, resolve_scale(scale, d));
+  return dispatch(dtype, d, q, k_blk, v_blk, out_part, lse_part, true, p, s,
+                  (int64_t)s.n_tiles * B * Hq, stream);
+}
+
+extern "C" int rattn_merge(float* out, float* lse, const float* blk_out, const float* blk_lse,
+                           int B, int H, int64_t Nq, int64_t Nb, int64_t row_off, int d,
+                           void* stream) {
+  if (B < 1 || H < 1 || Nq < 0 || Nb < 0 || row_off < 0) return RATTN_EINVAL;
+  // a pointer may be null only when no row is merged
+  if (Nb > 0 && (!out || !lse || !blk_out || !blk_lse)) return RATTN_EINVAL;
+  if (!supported_d(d)) return RATTN_EUNSUPPORTED;
+  if (row_off > Nq || Nb > Nq - row_off) return RATTN_EINVAL;
+  if (!aligned(out, 16) || !aligned(blk_out, 16) || !aligned(lse, 4) || !aligned(blk_lse, 4))
+    return RATTN_EINVAL;
+  if (!tensor_ok(B, Nq, H, d)) return RATTN_EUNSUPPORTED;
+  const int64_t threads = (int64_t)B * Nb * H * (d / 4);
+  if ((threads + 255) / 256 > INT32_MAX) return RATTN_EUNSUPPORTED;
+  hipError_t e = launch_merge(out, lse, blk_out, blk_lse, B, H, Nq, Nb, row_off, d,
+                              (hipStream_t)stream);
+  return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+}
+
+extern "C" const char* rattn_status_string(int status) {
+  switch (status) {
+    case RATTN_OK: return "ok";
+    case RATTN_EINVAL: return "invalid argument";
+    case RATTN_EUNSUPPORTED: return "unsupported configuration";
+    case RATTN_EHIP: return "HIP error while enqueueing work";
+    default: return "unknown status";
+  }
+}

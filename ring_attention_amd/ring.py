@@ -1,0 +1,89 @@
+"""One simulated device of the ring, run step by step on one GPU.
+
+Each step is one call of the step kernel (rattn_fwd_step) on the key/value
+shard the device holds at that step, followed by a log-sum-exp merge
+(rattn_merge) into the running (out, lse) -- the structure of the Twinkle
+forward pass ("Sequence parallel and Ring Attention", forward-pass section).
+The fused entry point (rattn_fwd) computes the same thing in one launch.
+
+Ring order: at step s device r holds the shard of device (r - s) mod W
+(ultralytics.com "Ring Attention": every device passes its block on to the
+next one and receives from the previous one).
+
+ZigZag step rules (Twinkle page, forward pass), for device r with shard
+[front; back] of chunks r and 2W-1-r:
+  step 0         all local queries x all local keys, causal
+  1 <= s <= r    all local queries x the front chunk of the received keys
+  s > r          the back half of the queries x all received keys
+Contiguous layout with causal masking (youngju.dev "Ring Attention" analysis,
+causal step): a block from a later device is skipped, the own block is
+masked, earlier blocks are fully visible.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding
+
+
+def shard_rows(N: int, W: int, zigzag: bool, rank: int):
+    """(start_position, length) runs of the rows device ``rank`` holds."""
+    if zigzag:
+        c = N // (2 * W)
+        return [(rank * c, c), ((2 * W - 1 - rank) * c, c)]
+    S = N // W
+    return [(rank * S, S)]
+
+
+def shard(x: torch.Tensor, W: int, zigzag: bool, rank: int) -> torch.Tensor:
+    """Rows of device ``rank`` of a natural-order [B, N, H, d] tensor, stored
+    contiguously in ring layout (front chunk, then back chunk for ZigZag).
+
+    This is data placement done before the timed work: in a real ring each
+    device already holds its shard in its own memory."""
+    N = x.shape[1]
+    parts = [x[:, a:a + n] for a, n in shard_rows(N, W, zigzag, rank)]
+    return torch.cat(parts, dim=1).contiguous() if len(parts) > 1 else parts[0].contiguous()
+
+
+def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag: bool,
+                       rank: int, causal: bool = True, scale: float | None = None):
+    """Run device ``rank``'s W ring steps; returns float32 (out, lse).
+
+    q_shard [B, Nq, Hq, d] is the device's query shard; k_shards[src] and
+    v_shards[src] are the shards every device would send (see ``shard``).
+    """
+    N = sum(k.shape[1] for k in k_shards)
+    B, Nq, Hq, d = q_shard.shape
+    out = lse = None
+    q_runs = shard_rows(N, W, zigzag, rank)
+    for s in range(W):
+        src = (rank - s) % W
+        k_runs = shard_rows(N, W, zigzag, src)
+        kb, vb = k_shards[src], v_shards[src]
+        row_off = 0
+        qv, qr, kr, step_causal = q_shard, q_runs, k_runs, causal
+        if zigzag and causal:
+            c = N // (2 * W)
+            if s == 0:
+                pass
+            elif s <= rank:
+                kb, vb = kb[:, :c], vb[:, :c]
+                kr, step_causal = k_runs[:1], False
+            else:
+                qv, qr, row_off, step_causal = q_shard[:, c:], q_runs[1:], c, False
+        elif causal:
+            if src > rank:
+                continue
+            step_causal = src == rank
+        if not qv.is_contiguous():
+            qv = qv.contiguous()
+        if not kb.is_contiguous():
+            kb, vb = kb.contiguous(), vb.contiguous()
+        if out is None:
+            # the first step writes the running result directly
+            out, lse = binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale)
+            continue
+        bo, bl = binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale)
+        binding.merge(out, lse, bo, bl, row_off=row_off)
+    return out, lse

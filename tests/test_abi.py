@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: exports and host-side argument checks.
+
+Every call here is rejected (or has no work) before anything is enqueued, so
+these tests never launch a kernel.  Fake device pointers are plain aligned
+integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from ring_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rattn.h")
+
+OK, EINVAL, EUNSUP, EHIP = 0, -1, -2, -3
+P = [0x10000 * (i + 1) for i in range(8)]  # 16-byte aligned, never dereferenced
+
+
+def declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"RATTN_API\s+[\w\s\*]*?\b(rattn_\w+)\s*\(", text))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared() == set(binding.EXPORTS)
+
+
+def test_library_exports_exactly_the_header(rattn_lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.split()[1:2] == ["T"]}
+    assert syms == declared()
+    for name in declared():
+        assert hasattr(rattn_lib, name)
+
+
+def test_status_strings(rattn_lib):
+    for code in (OK, EINVAL, EUNSUP, EHIP, 12345):
+        s = binding.status_string(code)
+        assert isinstance(s, str) and s
+    assert binding.status_string(12345) == "unknown status"
+
+
+def fwd(lib, q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4], B=1, Hq=2, Hkv=2, Nq=64, N=64, d=64,
+        dtype=2, scale=0.0, causal=1, W=1, zigzag=0, rank=-1):
+    return lib.rattn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, scale, causal, W,
+                         zigzag, rank, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), EINVAL), (dict(lse=0), EINVAL), (dict(B=0), EINVAL), (dict(Hq=3, Hkv=2), EINVAL),
+    (dict(Hkv=0), EINVAL), (dict(d=48), EUNSUP), (dict(d=256), EUNSUP), (dict(dtype=3), EINVAL),
+    (dict(causal=2), EINVAL), (dict(zigzag=2), EINVAL), (dict(W=0), EINVAL), (dict(W=33), EUNSUP),
+    (dict(W=3, N=64, Nq=64), EINVAL), (dict(W=4, zigzag=1, N=68, Nq=68), EINVAL),
+    (dict(W=4, rank=4), EINVAL), (dict(W=4, rank=-2), EINVAL),
+    (dict(W=4, rank=-1, Nq=16), EINVAL), (dict(W=4, rank=1, Nq=64), EINVAL),
+    (dict(q=P[0] + 2), EINVAL), (dict(out=P[3] + 8), EINVAL), (dict(lse=P[4] + 2), EINVAL),
+    (dict(N=-4, Nq=-4), EINVAL), (dict(B=1 << 30, Hq=1 << 30, Hkv=1 << 30, N=1 << 20,
+                                       Nq=1 << 20, d=128), EUNSUP),
+])
+def test_fwd_rejects(rattn_lib, kw, status):
+    assert fwd(rattn_lib, **kw) == status
+
+
+def test_fwd_empty_is_ok_without_launch(rattn_lib):
+    assert fwd(rattn_lib, N=0, Nq=0) == OK
+    assert fwd(rattn_lib, N=0, Nq=0, W=4, zigzag=1) == OK
+    # empty tensors may come with null pointers
+    assert fwd(rattn_lib, q=0, k=0, v=0, out=0, lse=0, N=0, Nq=0) == OK
+    assert fwd(rattn_lib, k=0, N=64, Nq=64) == EINVAL
+
+
+def seg(a, b):
+    return (ctypes.c_int64 * 2)(a, b)
+
+
+def step(lib, Nq=32, Nk=32, qs=(0, 0), ql=(32, 0), ks=(0, 0), kl=(32, 0), d=128, dtype=1,
+         causal=1, q=P[0], out=P[3], nulls=False):
+    arrs = [None] * 4 if nulls else [seg(*qs), seg(*ql), seg(*ks), seg(*kl)]
+    return lib.rattn_fwd_step(q, P[1], P[2], out, P[4], 1, 4, 2, Nq, Nk, d, dtype, 0.0, causal,
+                              *arrs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nulls=True), EINVAL), (dict(q=0), EINVAL), (dict(ql=(30, 0)), EINVAL),
+    (dict(kl=(16, 8)), EINVAL), (dict(ql=(40, -8)), EINVAL), (dict(d=12), EUNSUP),
+    (dict(dtype=-1), EINVAL), (dict(causal=-1), EINVAL), (dict(out=P[3] + 4), EINVAL),
+])
+def test_fwd_step_rejects(rattn_lib, kw, status):
+    assert step(rattn_lib, **kw) == status
+
+
+def test_fwd_step_empty_is_ok_without_launch(rattn_lib):
+    assert step(rattn_lib, Nq=0, ql=(0, 0)) == OK
+    assert step(rattn_lib, Nq=0, ql=(0, 0), q=0, out=0) == OK
+
+
+def merge(lib, out=P[0], lse=P[1], bo=P[2], bl=P[3], B=1, H=2, Nq=8, Nb=4, off=0, d=64):
+    return lib.rattn_merge(out, lse, bo, bl, B, H, Nq, Nb, off, d, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=0), EINVAL), (dict(bl=0), EINVAL), (dict(B=0), EINVAL), (dict(Nb=-1), EINVAL),
+    (dict(off=5), EINVAL), (dict(off=-1), EINVAL), (dict(Nb=9), EINVAL), (dict(d=8), EUNSUP),
+    (dict(out=P[0] + 4), EINVAL), (dict(lse=P[1] + 1), EINVAL),
+])
+def test_merge_rejects(rattn_lib, kw, status):
+    assert merge(rattn_lib, **kw) == status
+
+
+def test_merge_empty_is_ok_without_launch(rattn_lib):
+    assert merge(rattn_lib, Nb=0) == OK
+    assert merge(rattn_lib, Nb=0, bo=0, bl=0) == OK
+
+
+def test_launch_error_maps_to_status_without_gpu(rattn_lib):
+    """With no GPU present, a valid call reports RATTN_EHIP instead of crashing."""
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: this check only runs where launches must fail")
+    assert merge(rattn_lib) == EHIP
+    assert fwd(rattn_lib) == EHIP
+
+
+def test_binding_checks_tensors_before_calling():
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        binding.fwd(q, q, q)  # CPU tensors are refused before any library call
+    with pytest.raises(ValueError):
+        binding.merge(q, torch.zeros(1, 4, 1), q, torch.zeros(1, 4, 1))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        binding.load_library(str(tmp_path / "librattn.so"))

@@ -1,0 +1,347 @@
+"""HIP path vs the fp64 oracle on identical seeded inputs (needs a GPU).
+
+Tolerances (stated for this method): max |dO| <= 1e-5 for float32 inputs and
+<= 2e-2 for bfloat16/float16 inputs, |dLSE| <= 1e-3.  Small workloads compare
+every output element; the long workloads compare seeded sampled rows plus
+forced edge rows (the first and last row of every chunk, the first and last
+position).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import layouts
+from ring_attention_amd import binding, ring, workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {torch.float32: 1e-5, torch.float16: 2e-2, torch.bfloat16: 2e-2}
+TOL_LSE = 1e-3
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def compare(out, lse, ref_o, ref_l, dtype, tol_o=None, what=""):
+    out = np.asarray(out, np.float64)
+    lse = np.asarray(lse, np.float64)
+    tol_o = TOL_O[dtype] if tol_o is None else tol_o
+    both_empty = np.isneginf(lse) & np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref_l)), f"{what}: empty rows differ"
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err_o = np.max(np.abs(out - ref_o)) if out.size else 0.0
+    fin = ~both_empty
+    err_l = np.max(np.abs(lse[fin] - ref_l[fin])) if fin.any() else 0.0
+    note(f"{what}: max|dO|={err_o:.3e} (tol {tol_o:g}) max|dLSE|={err_l:.3e}")
+    assert err_o <= tol_o, f"{what}: max|dO| {err_o} > {tol_o}"
+    assert err_l <= TOL_LSE, f"{what}: max|dLSE| {err_l} > {TOL_LSE}"
+    return err_o, err_l
+
+
+def host(t):
+    return t.detach().float().cpu().numpy() if t.dtype != torch.float32 else t.detach().cpu().numpy()
+
+
+def q_positions(N, W, zigzag, rank):
+    return np.arange(N) if rank < 0 else layouts.shard_positions(N, W, rank, zigzag)
+
+
+def run_full_check(q, k, v, causal, W, zigzag, rank, what, tol_o=None):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out, lse = binding.fwd(qd, kd, vd, causal=causal, n_ring_steps=W, zigzag=zigzag, rank=rank)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(q, k, v, causal=causal,
+                                    q_pos=q_positions(k.shape[1], W, zigzag, rank))
+    return compare(host(out), host(lse), ref_o, ref_l, q.dtype, tol_o, what)
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+
+
+def test_workload1_tiny_ring_simulation(gpu):
+    w = workloads.workload(1)
+    q, k, v = workloads.make_inputs(w)
+    note(f"case {w.name}")
+    run_full_check(q, k, v, w.causal, w.W, w.zigzag, w.rank, w.name)
+
+
+def test_workload2_single_head(gpu):
+    w = workloads.workload(2)
+    q, k, v = workloads.make_inputs(w)
+    note(f"case {w.name}")
+    run_full_check(q, k, v, w.causal, w.W, w.zigzag, w.rank, w.name)
+
+
+def test_workload3_batched_multihead_causal(gpu):
+    w = workloads.workload(3)
+    q, k, v = workloads.make_inputs(w)
+    note(f"case {w.name}")
+    run_full_check(q, k, v, w.causal, w.W, w.zigzag, w.rank, w.name)
+
+
+def forced_rows_zigzag(w, c):
+    """First/last row of every chunk the query tensor holds, first/last head."""
+    idx = set()
+    for start in range(0, w.Nq, c):
+        idx.update({start, start + c - 1})
+    idx.update({0, w.Nq - 1})
+    return [(0, i, h) for i in sorted(idx) for h in (0, w.Hq - 1)]
+
+
+def sampled_rows(w):
+    c = w.N // (2 * w.W)
+    rows = workloads.sample_rows(w.B, w.Nq, w.Hq, w.sampled_rows, seed=100 + w.index,
+                                 forced=forced_rows_zigzag(w, c))
+    # group rows of one key/value head, in position order, so concurrent oracle
+    # threads stream the same keys
+    order = np.lexsort((rows[:, 1], rows[:, 2] // (w.Hq // w.Hkv), rows[:, 0]))
+    return rows[order]
+
+
+def check_sampled(out, lse, q_host, k_host, v_host, rows, qpos, w, what):
+    o = out[rows[:, 0], rows[:, 1], rows[:, 2]]
+    l = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    ref_o, ref_l = oracle.attention(q_host, k_host, v_host, causal=w.causal, q_pos=qpos,
+                                    rows=rows)
+    return compare(host(o), host(l), ref_o, ref_l, q_host.dtype, what=what)
+
+
+@pytest.fixture(scope="module")
+def workload4_inputs(gpu):
+    w = workloads.workload(4)
+    q, k, v = workloads.make_inputs(w, device=gpu)
+    return w, q, k, v
+
+
+def test_workload4_fused(workload4_inputs):
+    w, q, k, v = workload4_inputs
+    note(f"case {w.name} fused")
+    out, lse = binding.fwd(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=w.rank)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w)
+    check_sampled(out.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu(), rows,
+                  layouts.zigzag_shard_positions(w.N, w.W, w.rank), w, w.name + " fused")
+
+
+def test_workload4_ring_steps_and_merge(workload4_inputs):
+    w, q, k, v = workload4_inputs
+    note(f"case {w.name} steps+merge")
+    ks = [ring.shard(k, w.W, True, r) for r in range(w.W)]
+    vs = [ring.shard(v, w.W, True, r) for r in range(w.W)]
+    out, lse = ring.ring_forward_steps(q, ks, vs, w.W, True, w.rank, causal=True)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w)
+    check_sampled(out.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu(), rows,
+                  layouts.zigzag_shard_positions(w.N, w.W, w.rank), w, w.name + " steps")
+    # fused and step-by-step agree closely on every row
+    fo, fl = binding.fwd(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=w.rank)
+    torch.cuda.synchronize()
+    d_o = (fo.float() - out).abs().max().item()
+    d_l = (fl - lse).abs().max().item()
+    note(f"fused vs steps: max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= 2e-2 and d_l <= 1e-3
+
+
+def test_workload5_long_context_gqa(gpu):
+    w = workloads.workload(5)
+    note(f"case {w.name}: generating inputs on the GPU")
+    q, k, v = workloads.make_inputs(w, device=gpu)
+    out, lse = binding.fwd(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=-1)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w)
+    ridx = torch.as_tensor(rows, device=gpu)
+    o = out[ridx[:, 0], ridx[:, 1], ridx[:, 2]].cpu()
+    l = lse[ridx[:, 0], ridx[:, 1], ridx[:, 2]].cpu()
+    q_sel = q[ridx[:, 0], ridx[:, 1], ridx[:, 2]].cpu()  # [n, d]
+    del out, lse, q
+    note(f"{w.name}: oracle on {len(rows)} rows")
+    k_host, v_host = k.cpu(), v.cpu()
+    group = w.Hq // w.Hkv
+    ref_o = np.zeros((len(rows), w.d))
+    ref_l = np.zeros(len(rows))
+    for g in range(w.Hkv):
+        sel = np.nonzero(rows[:, 2] // group == g)[0]
+        if len(sel) == 0:
+            continue
+        qg = q_sel[sel].reshape(1, len(sel), 1, w.d).contiguous()
+        kg = k_host[:, :, g:g + 1].contiguous()
+        vg = v_host[:, :, g:g + 1].contiguous()
+        ro, rl = oracle.attention(qg, kg, vg, causal=True, q_pos=rows[sel, 1])
+        ref_o[sel] = ro[0, :, 0]
+        ref_l[sel] = rl[0, :, 0]
+    compare(host(o), host(l), ref_o, ref_l, torch.bfloat16, what=w.name)
+
+
+# --------------------------------------------------------------------------
+# edge cases and variants at sizes the oracle checks in full
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dtypes_and_head_dims_ragged(gpu, dtype, d, causal):
+    # 200 rows: not a multiple of any tile size
+    q, k, v = workloads.make_qkv(2, 200, 200, 4, 2, d, dtype, seed=7 + d)
+    run_full_check(q, k, v, causal, 1, False, -1, f"dtype={dtype} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("W,zigzag", [(1, False), (2, False), (3, False), (4, False), (1, True),
+                                      (2, True), (3, True), (4, True)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ring_layouts_all_ranks(gpu, W, zigzag, dtype):
+    N = 2 * W * 40 if zigzag else W * 70  # chunks shorter than a tile, ragged
+    q, k, v = workloads.make_qkv(1, N, N, 2, 1, 64, dtype, seed=11 * W + zigzag)
+    run_full_check(q, k, v, True, W, zigzag, -1, f"W={W} zigzag={zigzag} all ranks")
+    for r in range(W):
+        qs = ring.shard(q, W, zigzag, r)
+        run_full_check(qs, k, v, True, W, zigzag, r, f"W={W} zigzag={zigzag} rank={r}")
+
+
+@pytest.mark.parametrize("W,zigzag", [(2, False), (3, True), (4, True)])
+def test_ring_steps_equal_oracle(gpu, W, zigzag):
+    N = 2 * W * 96 if zigzag else W * 160
+    q, k, v = workloads.make_qkv(1, N, N, 4, 2, 128, torch.bfloat16, seed=5 + W)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ks = [ring.shard(kd, W, zigzag, r) for r in range(W)]
+    vs = [ring.shard(vd, W, zigzag, r) for r in range(W)]
+    for r in range(W):
+        out, lse = ring.ring_forward_steps(ring.shard(qd, W, zigzag, r), ks, vs, W, zigzag, r)
+        torch.cuda.synchronize()
+        qs = ring.shard(q, W, zigzag, r)
+        ref_o, ref_l = oracle.attention(qs, k, v, causal=True,
+                                        q_pos=layouts.shard_positions(N, W, r, zigzag))
+        compare(host(out), host(lse), ref_o, ref_l, torch.bfloat16,
+                what=f"steps W={W} zigzag={zigzag} rank={r}")
+
+
+def test_noncausal_result_independent_of_schedule(gpu):
+    q, k, v = workloads.make_qkv(1, 512, 512, 2, 2, 128, torch.float16, seed=3, device=gpu)
+    base, base_l = binding.fwd(q, k, v)
+    for W, zz in ((2, False), (4, True), (8, True)):
+        o, l = binding.fwd(q, k, v, n_ring_steps=W, zigzag=zz)
+        assert (o.float() - base.float()).abs().max().item() <= 2e-3
+        assert (l - base_l).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_large_magnitude_scores(gpu, dtype):
+    g = torch.Generator().manual_seed(21)
+    q = (torch.randn(1, 300, 2, 64, generator=g) * 10).to(dtype)
+    k = (torch.randn(1, 300, 2, 64, generator=g) * 10).to(dtype)
+    v = torch.randn(1, 300, 2, 64, generator=g).to(dtype)
+    # float32: the score error grows with |s| (~1e3 here), so allow 1e-4
+    tol = 1e-4 if dtype == torch.float32 else None
+    run_full_check(q, k, v, True, 1, False, -1, f"large scores {dtype}", tol_o=tol)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 1), (6, 6)])
+def test_gqa_head_mapping(gpu, Hq, Hkv):
+    q, k, v = workloads.make_qkv(1, 256, 256, Hq, Hkv, 128, torch.bfloat16, seed=Hq * 10 + Hkv)
+    run_full_check(q, k, v, True, 1, False, -1, f"GQA {Hq}/{Hkv}")
+
+
+def test_single_row_and_single_key(gpu):
+    for dtype in (torch.float32, torch.bfloat16):
+        q, k, v = workloads.make_qkv(1, 1, 1, 1, 1, 128, dtype, seed=2)
+        run_full_check(q, k, v, True, 1, False, -1, f"N=1 {dtype}")
+
+
+def test_page_triton_test_shape(gpu):
+    """The yz520gzy chapter's kernel test: seed 42, (B,H,N,D) = (2,4,1024,64)
+    fp16, non-causal, gate max|diff| < 1e-2 against softmax attention."""
+    torch.manual_seed(42)
+    B, H, N, D = 2, 4, 1024, 64
+    q = torch.randn(B, H, N, D, device="cuda", dtype=torch.float16)
+    k = torch.randn(B, H, N, D, device="cuda", dtype=torch.float16)
+    v = torch.randn(B, H, N, D, device="cuda", dtype=torch.float16)
+    qs, ks, vs = (x.transpose(1, 2).contiguous() for x in (q, k, v))  # to (B, N, H, D)
+    out, lse = binding.fwd(qs, ks, vs)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(qs.cpu(), ks.cpu(), vs.cpu())
+    err = compare(host(out), host(lse), ref_o, ref_l, torch.float16, tol_o=1e-2,
+                  what="page Triton-test shape")[0]
+    assert err < 1e-2
+
+
+# --------------------------------------------------------------------------
+# step kernel and merge kernel on their own
+
+
+def test_step_rows_without_visible_keys(gpu):
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_qkv(1, 130, 70, 2, 2, 64, torch.bfloat16, seed=9)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    # queries at positions 0..64 and 1000..1064; keys at 30..99
+    q_segs, k_segs = [(0, 65), (1000, 65)], [(30, 70)]
+    out, lse = binding.fwd_step(qd, kd, vd, True, q_segs, k_segs)
+    torch.cuda.synchronize()
+    qpos = np.concatenate([np.arange(0, 65), np.arange(1000, 1065)])
+    ref_o, ref_l = oracle.attention(q, k, v, causal=True, q_pos=qpos, k_pos=np.arange(30, 100))
+    compare(host(out), host(lse), ref_o, ref_l, torch.bfloat16, what="step, empty rows")
+    assert np.isneginf(host(lse)[0, :30]).all() and (host(out)[0, :30] == 0).all()
+
+
+def test_step_with_no_keys(gpu):
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_qkv(1, 40, 0, 1, 1, 32, torch.float16, seed=1, device=dev)
+    out, lse = binding.fwd_step(q, k, v, False, [(0, 40)], [(0, 0)])
+    torch.cuda.synchronize()
+    assert (out == 0).all() and torch.isneginf(lse).all()
+
+
+def test_step_two_key_segments(gpu):
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_qkv(2, 150, 190, 4, 4, 128, torch.float16, seed=31)
+    q_segs, k_segs = [(500, 150)], [(0, 90), (600, 100)]
+    out, lse = binding.fwd_step(q.to(dev), k.to(dev), v.to(dev), True, q_segs, k_segs)
+    torch.cuda.synchronize()
+    kpos = np.concatenate([np.arange(0, 90), np.arange(600, 700)])
+    ref_o, ref_l = oracle.attention(q, k, v, causal=True, q_pos=np.arange(500, 650), k_pos=kpos)
+    compare(host(out), host(lse), ref_o, ref_l, torch.float16, what="step, two key runs")
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_merge_kernel(gpu, d):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(d)
+    B, Nq, H, Nb, off = 2, 50, 3, 20, 17
+    o = rng.standard_normal((B, Nq, H, d)).astype(np.float32)
+    l = (rng.standard_normal((B, Nq, H)) * 5).astype(np.float32)
+    bo = rng.standard_normal((B, Nb, H, d)).astype(np.float32)
+    bl = (rng.standard_normal((B, Nb, H)) * 5).astype(np.float32)
+    l[0, off:off + 3] = -np.inf          # empty running rows
+    o[0, off:off + 3] = 0
+    bl[0, 2:5] = -np.inf                 # empty block rows (2 overlap the above)
+    bo[0, 2:5] = 0
+    od, ld = torch.from_numpy(o).to(dev), torch.from_numpy(l).to(dev)
+    binding.merge(od, ld, torch.from_numpy(bo).to(dev), torch.from_numpy(bl).to(dev), row_off=off)
+    torch.cuda.synchronize()
+    ref_o, ref_l = o.astype(np.float64).copy(), l.astype(np.float64).copy()
+    mo, ml = oracle.merge(ref_o[:, off:off + Nb], ref_l[:, off:off + Nb], bo, bl)
+    ref_o[:, off:off + Nb], ref_l[:, off:off + Nb] = mo, ml
+    got_o, got_l = od.cpu().numpy(), ld.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    fin = ~np.isneginf(ref_l)
+    assert np.max(np.abs(got_o - ref_o)) <= 1e-5
+    assert np.max(np.abs(got_l[fin] - ref_l[fin])) <= 1e-5
+    # rows outside [off, off+Nb) are untouched, bit for bit
+    assert np.array_equal(got_o[:, :off], o[:, :off]) and np.array_equal(got_l[:, :off], l[:, :off])
+
+
+def test_runs_on_a_side_stream_and_is_deterministic(gpu):
+    q, k, v = workloads.make_qkv(1, 1000, 1000, 4, 4, 128, torch.bfloat16, seed=4, device=gpu)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1, l1 = binding.fwd(q, k, v, causal=True, n_ring_steps=4, zigzag=True)
+        o2, l2 = binding.fwd(q, k, v, causal=True, n_ring_steps=4, zigzag=True)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
