@@ -79,13 +79,79 @@ double oracle_bf16_to_double(uint16_t b)
     return (double)x;
 }
 
+/* Tables of the two decoders above, one entry per 16-bit pattern, so that the
+ * inner loops read a table instead of calling the decoder. */
+static double lut_f16[65536], lut_bf16[65536];
+static int lut_ready;
+
+static void build_luts(void)
+{
+    if (lut_ready) return;
+    for (uint32_t b = 0; b < 65536; ++b) {
+        lut_f16[b] = oracle_f16_to_double((uint16_t)b);
+        lut_bf16[b] = oracle_bf16_to_double((uint16_t)b);
+    }
+    lut_ready = 1;
+}
+
 static double load(const void *base, int64_t idx, int dtype)
 {
     switch (dtype) {
     case ORACLE_F32: return (double)((const float *)base)[idx];
-    case ORACLE_F16: return oracle_f16_to_double(((const uint16_t *)base)[idx]);
-    default:         return oracle_bf16_to_double(((const uint16_t *)base)[idx]);
+    case ORACLE_F16: return lut_f16[((const uint16_t *)base)[idx]];
+    default:         return lut_bf16[((const uint16_t *)base)[idx]];
     }
+}
+
+/*
+ * One query row (b, i, hq): the definition above, two passes.  `dtype` is a
+ * compile-time constant at each call site below, so the decoder switch in
+ * load() folds away; the arithmetic is the same for every dtype.
+ */
+static inline __attribute__((always_inline)) void
+attend_row(const void *q, const void *k, const void *v, const int dtype, int Hq, int Hkv,
+           int64_t Nq, int64_t Nk, int d, const int64_t *q_pos, const int64_t *k_pos,
+           int causal, double scale, int group, int64_t b, int64_t i, int64_t hq,
+           double *s, double *qrow, double *acc, double *o, double *lse_r)
+{
+    const int64_t g = hq / group;
+    for (int t = 0; t < d; ++t)
+        qrow[t] = load(q, ((b * Nq + i) * Hq + hq) * d + t, dtype);
+
+    /* pass 1: scores of the visible keys and their maximum */
+    double M = -INFINITY;
+    int64_t n_visible = 0;
+    for (int64_t j = 0; j < Nk; ++j) {
+        if (causal && k_pos[j] > q_pos[i]) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        double dot = 0.0;
+        const int64_t kbase = ((b * Nk + j) * Hkv + g) * d;
+        for (int t = 0; t < d; ++t)
+            dot += qrow[t] * load(k, kbase + t, dtype);
+        s[j] = scale * dot;
+        if (s[j] > M) M = s[j];
+        ++n_visible;
+    }
+    if (n_visible == 0) {
+        for (int t = 0; t < d; ++t) o[t] = 0.0;
+        *lse_r = -INFINITY;
+        return;
+    }
+    /* pass 2: normaliser and weighted sum of values */
+    double Z = 0.0;
+    for (int t = 0; t < d; ++t) acc[t] = 0.0;
+    for (int64_t j = 0; j < Nk; ++j) {
+        if (causal && k_pos[j] > q_pos[i]) continue;
+        const double w = exp(s[j] - M);
+        Z += w;
+        const int64_t vbase = ((b * Nk + j) * Hkv + g) * d;
+        for (int t = 0; t < d; ++t)
+            acc[t] += w * load(v, vbase + t, dtype);
+    }
+    for (int t = 0; t < d; ++t) o[t] = acc[t] / Z;
+    *lse_r = M + log(Z);
 }
 
 /*
@@ -105,12 +171,14 @@ int oracle_attention_rows(const void *q, const void *k, const void *v, int dtype
                           double *out, double *lse, int n_threads)
 {
     if (!q || !k || !v || !out || !lse || B < 1 || Hq < 1 || Hkv < 1 || d < 1 ||
-        Nq < 0 || Nk < 0 || Hq % Hkv != 0 || (causal && (!q_pos || !k_pos)))
+        Nq < 0 || Nk < 0 || Hq % Hkv != 0 || (causal && (!q_pos || !k_pos)) ||
+        dtype < ORACLE_F32 || dtype > ORACLE_BF16)
         return -1;
     if (!rows && n_rows != (int64_t)B * Nq * Hq)
         return -1;
     const int group = Hq / Hkv;
     int bad = 0;
+    build_luts();  /* before the parallel region: no concurrent writers */
 #ifdef _OPENMP
     if (n_threads > 0)
         omp_set_num_threads(n_threads);
@@ -126,7 +194,7 @@ int oracle_attention_rows(const void *q, const void *k, const void *v, int dtype
         if (!s || !qrow || !acc) {
             bad = 1;
         } else {
-#pragma omp for schedule(dynamic, 16)
+#pragma omp for schedule(dynamic, 4)
             for (int64_t r = 0; r < n_rows; ++r) {
                 int64_t b, i, hq;
                 if (rows) {
@@ -138,45 +206,21 @@ int oracle_attention_rows(const void *q, const void *k, const void *v, int dtype
                     bad = 1;
                     continue;
                 }
-                const int64_t g = hq / group;
-                for (int t = 0; t < d; ++t)
-                    qrow[t] = load(q, ((b * Nq + i) * Hq + hq) * d + t, dtype);
-
-                /* pass 1: scores of the visible keys and their maximum */
-                double M = -INFINITY;
-                int64_t n_visible = 0;
-                for (int64_t j = 0; j < Nk; ++j) {
-                    if (causal && k_pos[j] > q_pos[i]) {
-                        s[j] = -INFINITY;
-                        continue;
-                    }
-                    double dot = 0.0;
-                    const int64_t kbase = ((b * Nk + j) * Hkv + g) * d;
-                    for (int t = 0; t < d; ++t)
-                        dot += qrow[t] * load(k, kbase + t, dtype);
-                    s[j] = scale * dot;
-                    if (s[j] > M) M = s[j];
-                    ++n_visible;
-                }
                 double *o = out + r * d;
-                if (n_visible == 0) {
-                    for (int t = 0; t < d; ++t) o[t] = 0.0;
-                    lse[r] = -INFINITY;
-                    continue;
+                switch (dtype) {
+                case ORACLE_F32:
+                    attend_row(q, k, v, ORACLE_F32, Hq, Hkv, Nq, Nk, d, q_pos, k_pos, causal,
+                               scale, group, b, i, hq, s, qrow, acc, o, lse + r);
+                    break;
+                case ORACLE_F16:
+                    attend_row(q, k, v, ORACLE_F16, Hq, Hkv, Nq, Nk, d, q_pos, k_pos, causal,
+                               scale, group, b, i, hq, s, qrow, acc, o, lse + r);
+                    break;
+                default:
+                    attend_row(q, k, v, ORACLE_BF16, Hq, Hkv, Nq, Nk, d, q_pos, k_pos, causal,
+                               scale, group, b, i, hq, s, qrow, acc, o, lse + r);
+                    break;
                 }
-                /* pass 2: normaliser and weighted sum of values */
-                double Z = 0.0;
-                for (int t = 0; t < d; ++t) acc[t] = 0.0;
-                for (int64_t j = 0; j < Nk; ++j) {
-                    if (causal && k_pos[j] > q_pos[i]) continue;
-                    const double w = exp(s[j] - M);
-                    Z += w;
-                    const int64_t vbase = ((b * Nk + j) * Hkv + g) * d;
-                    for (int t = 0; t < d; ++t)
-                        acc[t] += w * load(v, vbase + t, dtype);
-                }
-                for (int t = 0; t < d; ++t) o[t] = acc[t] / Z;
-                lse[r] = M + log(Z);
             }
         }
         free(s);

@@ -509,7 +509,7 @@ MUTATIONS = {
     "causal_off_by_one": ("k_pos[j] > q_pos[i]", "k_pos[j] >= q_pos[i]"),
     "dropped_scale": ("s[j] = scale * dot;", "s[j] = dot;"),
     "wrong_gqa_map": ("const int64_t g = hq / group;", "const int64_t g = hq % Hkv;"),
-    "lse_without_max": ("lse[r] = M + log(Z);", "lse[r] = log(Z);"),
+    "lse_without_max": ("*lse_r = M + log(Z);", "*lse_r = log(Z);"),
     "k_used_as_v": ("acc[t] += w * load(v, vbase + t, dtype);",
                     "acc[t] += w * load(k, vbase + t, dtype);"),
     "f16_exponent_off": ("e - 25);", "e - 24);"),
