@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of the workload the CPU oracle times")
     return ap.parse_args()
 
@@ -131,8 +131,9 @@ def main():
     pairs = sum(step_pairs)
     flop_per_step = 4 * d * Hq * w.B * pairs
 
-    def one_step(timer=None):
-        return ring.ring_forward_steps(q, ks, vs, W, True, rank, causal=True)
+    def one_step(hook=None):
+        kw = {} if hook is None else {"hook": hook}
+        return ring.ring_forward_steps(q, ks, vs, W, True, rank, causal=True, **kw)
 
     for _ in range(args.warmup):
         one_step()
@@ -153,14 +154,12 @@ def main():
     # per-launch timing of the dominant kernel (the step kernel), on the same stream
     kern = Timer(torch)
     merge_t = Timer(torch)
-    orig_step, orig_merge = binding.fwd_step, binding.merge
-    try:
-        ring.binding.fwd_step = lambda *a, **kw: kern(lambda: orig_step(*a, **kw))
-        ring.binding.merge = lambda *a, **kw: merge_t(lambda: orig_merge(*a, **kw))
-        for _ in range(args.steps):
-            one_step()
-    finally:
-        ring.binding.fwd_step, ring.binding.merge = orig_step, orig_merge
+
+    def hook(kind, fn):
+        return (kern if kind == "step" else merge_t)(fn)
+
+    for _ in range(args.steps):
+        one_step(hook)
     n_launch = len(kern.pairs)
     kern_ms = kern.total_ms() / n_launch
     merge_ms = merge_t.total_ms() / max(1, len(merge_t.pairs))

@@ -46,12 +46,19 @@ def shard(x: torch.Tensor, W: int, zigzag: bool, rank: int) -> torch.Tensor:
     return torch.cat(parts, dim=1).contiguous() if len(parts) > 1 else parts[0].contiguous()
 
 
+def _direct(kind, fn):
+    return fn()
+
+
 def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag: bool,
-                       rank: int, causal: bool = True, scale: float | None = None):
+                       rank: int, causal: bool = True, scale: float | None = None,
+                       hook=_direct):
     """Run device ``rank``'s W ring steps; returns float32 (out, lse).
 
     q_shard [B, Nq, Hq, d] is the device's query shard; k_shards[src] and
     v_shards[src] are the shards every device would send (see ``shard``).
+    hook(kind, fn) wraps every library call ("step" or "merge") and must
+    return fn(); a benchmark uses it to time the launches.
     """
     N = sum(k.shape[1] for k in k_shards)
     B, Nq, Hq, d = q_shard.shape
@@ -82,8 +89,9 @@ def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag
             kb, vb = kb.contiguous(), vb.contiguous()
         if out is None:
             # the first step writes the running result directly
-            out, lse = binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale)
+            out, lse = hook("step", lambda: binding.fwd_step(qv, kb, vb, step_causal, qr, kr,
+                                                             scale))
             continue
-        bo, bl = binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale)
-        binding.merge(out, lse, bo, bl, row_off=row_off)
+        bo, bl = hook("step", lambda: binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale))
+        hook("merge", lambda: binding.merge(out, lse, bo, bl, row_off=row_off))
     return out, lse
