@@ -116,21 +116,50 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   const E* kbase = k + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D;
   const E* vbase = v + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D;
 
+  // Per-thread byte offsets of its 16-byte chunks inside a tile, relative to
+  // the tile's first row (the tile base is uniform, so every load is one
+  // global_load with a scalar base and a 32-bit vector offset).  K chunks run
+  // along rows (coalesced); V chunks give each lane one key (for the
+  // transposed LDS store).
+  uint32_t koff[CH], voff[CH];
+  int krow_of[CH], vrow_of[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int ci = tid + kThreads * i;
+    krow_of[i] = ci / CPR;
+    vrow_of[i] = ci % kBc;
+    koff[i] = (uint32_t)((krow_of[i] * kv_stride + (ci % CPR) * 8) * sizeof(E));
+    voff[i] = (uint32_t)((vrow_of[i] * kv_stride + (ci / kBc) * 8) * sizeof(E));
+  }
+  const uint32_t row_bytes = (uint32_t)(kv_stride * sizeof(E));
+
   uint4 kreg[CH], vreg[CH];
 
   auto load_tile = [&](const TileCursor& c) {
     const int64_t krow0 = c.run.row0 + c.t * kBc;
     const int64_t rem = c.run.len - c.t * kBc;
-    const int krows = rem < kBc ? (int)rem : kBc;
+    const char* kt = (const char*)(kbase + krow0 * kv_stride);
+    const char* vt = (const char*)(vbase + krow0 * kv_stride);
+    if (rem >= kBc) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int ci = tid + kThreads * i;
-      const int kr = ci / CPR, kc = ci % CPR;    // K: 16-byte chunks along a row
-      kreg[i] = kr < krows ? *(const uint4*)(kbase + (krow0 + kr) * kv_stride + kc * 8)
-                           : make_uint4(0, 0, 0, 0);
-      const int vr = ci % kBc, vc = ci / kBc;    // V: one key per lane
-      vreg[i] = vr < krows ? *(const uint4*)(vbase + (krow0 + vr) * kv_stride + vc * 8)
-                           : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < CH; ++i) {
+        kreg[i] = *(const uint4*)(kt + koff[i]);
+        vreg[i] = *(const uint4*)(vt + voff[i]);
+      }
+    } else {
+      // ragged last tile of a run: rows past its end read the last row
+      // (in bounds) and are zeroed, so no score or value comes from them
+      const int krows = (int)rem;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int kx = krow_of[i] < krows ? 0 : krow_of[i] - (krows - 1);
+        const int vx = vrow_of[i] < krows ? 0 : vrow_of[i] - (krows - 1);
+        const uint4 ka = *(const uint4*)(kt + koff[i] - (uint32_t)kx * row_bytes);
+        const uint4 va = *(const uint4*)(vt + voff[i] - (uint32_t)vx * row_bytes);
+        const uint32_t km = kx ? 0u : ~0u, vm = vx ? 0u : ~0u;
+        kreg[i] = make_uint4(ka.x & km, ka.y & km, ka.z & km, ka.w & km);
+        vreg[i] = make_uint4(va.x & vm, va.y & vm, va.z & vm, va.w & vm);
+      }
     }
   };
   auto store_tile = [&](int buf) {
@@ -192,17 +221,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
             sacc[kb][r] = kk < lim ? sacc[kb][r] : kNegInf;
           }
       }
-      // online softmax
+      // online softmax.  The running max only moves when some row's tile
+      // max exceeds it by more than kRescaleSlack (base-2 units); otherwise
+      // scores are exponentiated against the stale max, so p <= 2^slack,
+      // and the O/l rescale is skipped for the whole wave.  Exact in exact
+      // arithmetic: O and l always share one reference max.
       float mt = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt * p.c);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
+      mt = pair_max(mt);
+      const float m_cand = mt * p.c;
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, m_cand);
+        const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
       float rs = 0.f;
       v8 pf[4];
 #pragma unroll
@@ -213,11 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
           rs += pr;
           pf[2 * kb + (r >> 3)][r & 7] = to_elem<TT>(pr);
         }
-      l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      l_run += rs;
       // O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -233,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   }
 
   // ---- epilogue: O / l, LSE = m ln2 + ln l --------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (!q_valid) return;
   const bool seen = l_tot > 0.f;
   const float inv = seen ? 1.f / l_tot : 0.f;
@@ -279,7 +316,6 @@ hipError_t launch_d(int d, const void* q, const void* k, const void* v, void* ou
   switch (d) {
     case 32: return launch_t<TT, 32>(q, k, v, out, lse, out_f32, p, s, stream);
     case 64: return launch_t<TT, 64>(q, k, v, out, lse, out_f32, p, s, stream);
-    case 128: return launch_t<TT, 128>(q, k, v, out, lse, out_f32, p, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -289,6 +325,7 @@ hipError_t launch_d(int d, const void* q, const void* k, const void* v, void* ou
 hipError_t launch_fwd_mfma(int dtype, int d, const void* q, const void* k, const void* v,
                            void* out, float* lse, bool out_f32, const FwdParams& p,
                            const Sched& s, hipStream_t stream) {
+  if (d == 128) return launch_fwd_mfma128(dtype, q, k, v, out, lse, out_f32, p, s, stream);
   switch (dtype) {
     case 1: return launch_d<F16>(d, q, k, v, out, lse, out_f32, p, s, stream);
     case 2: return launch_d<Bf16>(d, q, k, v, out, lse, out_f32, p, s, stream);

@@ -52,6 +52,25 @@ __device__ __forceinline__ typename TT::elem to_elem(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lanes l and l^32 hold the two halves of one query's keys in the 32x32 MFMA
+// accumulator layout.  v_permlane32_swap with both operands = x returns, in
+// each lane, x of lane l%32 and x of lane l%32+32 (one per result, in an
+// order that depends on the half); max and sum of the two are symmetric, so
+// they do not depend on that order.  A VALU exchange: no LDS round trip.
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Lazy rescaling threshold, in base-2 units of the scaled score.
+constexpr float kRescaleSlack = 8.f;
+
 // Number of leading keys of a key tile visible to one query: keys kk < limit
 // are visible.  `rows` keys are present in the tile; under the causal rule
 // key kk (at position kpos0 + kk) is visible iff kk <= qpos - kpos0 = rel.

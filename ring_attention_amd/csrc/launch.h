@@ -14,7 +14,12 @@ hipError_t launch_fwd_generic(int dtype, int d, const void* q, const void* k, co
                               void* out, float* lse, bool out_f32, const FwdParams& p,
                               const Sched& s, hipStream_t stream);
 
-// 16-bit inputs, d in {32, 64, 128}.
+// 16-bit inputs, d = 128 (direct-to-LDS tiles, transposing V reads).
+hipError_t launch_fwd_mfma128(int dtype, const void* q, const void* k, const void* v, void* out,
+                              float* lse, bool out_f32, const FwdParams& p, const Sched& s,
+                              hipStream_t stream);
+
+// 16-bit inputs, d in {32, 64, 128} (d = 128 is routed to launch_fwd_mfma128).
 hipError_t launch_fwd_mfma(int dtype, int d, const void* q, const void* k, const void* v,
                            void* out, float* lse, bool out_f32, const FwdParams& p,
                            const Sched& s, hipStream_t stream);
