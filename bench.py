@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of the workload the CPU oracle times")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy, whose byte "
+                         "counters calibrate the kernels' FETCH_SIZE/WRITE_SIZE readings")
     return ap.parse_args()
 
 
@@ -118,6 +121,13 @@ def main():
         sys.exit(1)
     binding.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads exactly 1 GiB, writes exactly 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     w = workloads.workload(4)
     W, rank, N, d, Hq = w.W, w.rank, w.N, w.d, w.Hq
     c = N // (2 * W)

@@ -37,11 +37,23 @@ namespace rattn {
 namespace {
 
 constexpr int D = 128;
-constexpr int kBc = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 wavefronts x 32 query rows
 constexpr int kRowBytes = D * 2;
-constexpr int kTileBytes = kBc * kRowBytes;            // 16 KB
-constexpr int kBufBytes = 2 * kTileBytes;              // K + V
+
+// Keys per tile: 64 (two resident workgroups per CU) or 32 (three).
+#ifndef RATTN_D128_BC
+#define RATTN_D128_BC 64
+#endif
+constexpr int BC = RATTN_D128_BC;
+static_assert(BC == 32 || BC == 64, "tile width");
+// A K+V buffer holds 2*BC rows of 256 bytes; each wave moves BC/16 1-KB DMA
+// blocks per tensor.
+constexpr int kTileBytes = BC * kRowBytes;
+constexpr int kBufBytes = 2 * kTileBytes;
+constexpr int NKB = BC / 32;   // 32-key score blocks
+constexpr int NU = BC / 16;    // 16-key PV steps
+constexpr int NDMA = BC / 16;  // DMA blocks per wave per tensor
+constexpr int kWavesPerEu = BC == 64 ? 2 : 3;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -62,8 +74,10 @@ __device__ __forceinline__ v4s read_tr(const char* lds, uint32_t off) {
           (__attribute__((address_space(3))) char*)(lds_void*)(lds + off)));
 }
 
+static_assert(kThreads / 64 * 32 == kMfma128Br, "schedule built for this tile height");
+
 template <typename TT, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
+__global__ __launch_bounds__(kThreads, kWavesPerEu) void fwd_mfma128_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
     FwdParams p, Sched s) {
@@ -72,6 +86,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   using v4 = typename TT::v4;
   constexpr int KS = D / 16;  // 8 k-steps of S
   constexpr int DB = D / 32;  // 4 row blocks of O^T
+  constexpr int kBc = BC;
 
   __shared__ __attribute__((aligned(1024))) char smem0[kBufBytes];
   __shared__ __attribute__((aligned(1024))) char smem1[kBufBytes];
@@ -122,29 +137,48 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   const char* kbase = (const char*)(k + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D);
   const char* vbase = (const char*)(v + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D);
   const uint32_t row_bytes = (uint32_t)(kv_stride * sizeof(E));
-  // this lane's row inside each 4-row DMA block, and the chunk it fetches
-  const int dma_r = lane >> 4;  // 0..3
-  const int dma_slot = l16;
+  // Tile rows handled by this wave: DMA blocks n = NDMA*wave + i,
+  // rows 4n + lane/16; lane l writes LDS slot l%16 of its row and fetches
+  // the logical chunk that belongs there.  Per-lane byte offsets from the
+  // tile's first row are fixed, so each DMA is one scalar tile base plus a
+  // 32-bit lane offset.
+  uint32_t kdma_off[NDMA], vdma_off[NDMA];
+  int dma_row[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int r = 4 * (NDMA * wave + i) + (lane >> 4);
+    dma_row[i] = r;
+    kdma_off[i] = (uint32_t)r * row_bytes + 16 * (l16 ^ (r & 15));
+    vdma_off[i] = (uint32_t)r * row_bytes + 16 * (l16 ^ (4 * (r & 3)));
+  }
 
-  // Tile rows handled by this wave: blocks n = 4*wave + i, rows 4n + dma_r.
   auto issue_tile = [&](const TileCursor& c, char* lk) {
     const int64_t krow0 = c.run.row0 + c.t * kBc;
     const int64_t rem = c.run.len - c.t * kBc;
-    const int last = (rem < kBc ? (int)rem : kBc) - 1;
     const char* kt = kbase + krow0 * (int64_t)row_bytes;
     const char* vt = vbase + krow0 * (int64_t)row_bytes;
     char* lv = lk + kTileBytes;
+    if (rem >= kBc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = 4 * wave + i;
-      const int r = 4 * n + dma_r;
-      const int rr = r <= last ? r : last;  // ragged tile: repeat the last row
-      const int kc = dma_slot ^ (r & 15);
-      const int vc = dma_slot ^ (4 * (r & 3));
-      __builtin_amdgcn_global_load_lds(kt + (uint32_t)rr * row_bytes + 16 * kc,
-                                       lds_at(lk, n * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt + (uint32_t)rr * row_bytes + 16 * vc,
-                                       lds_at(lv, n * 1024), 16, 0, 0);
+      for (int i = 0; i < NDMA; ++i) {
+        const int n = NDMA * wave + i;
+        __builtin_amdgcn_global_load_lds(kt + kdma_off[i], lds_at(lk, n * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + vdma_off[i], lds_at(lv, n * 1024), 16, 0, 0);
+      }
+    } else {
+      // ragged last tile of a run: rows past its end repeat the last row
+      // (finite values; their scores are masked, so p = 0 for them)
+      const uint32_t back_unit = row_bytes;
+      const int last = (int)rem - 1;
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int n = NDMA * wave + i;
+        const uint32_t back = dma_row[i] > last ? (uint32_t)(dma_row[i] - last) * back_unit : 0u;
+        __builtin_amdgcn_global_load_lds(kt + (kdma_off[i] - back), lds_at(lk, n * 1024), 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds(vt + (vdma_off[i] - back), lds_at(lv, n * 1024), 16,
+                                         0, 0);
+      }
     }
   };
 
@@ -184,21 +218,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
     const bool wave_sees = wave_active && (!s.causal || kpos0 <= wave_qhi);
     if (wave_sees) {
       const char* lb = cur_buf;
-      // S^T = K Q^T
-      f32x16 sacc[2];
+      // S^T = K Q^T.  All K fragments of the tile are requested before the
+      // first MFMA so the LDS latency is paid once per tile, and the 32-key
+      // accumulator chains alternate.
+      v8 kf[NKB][KS];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sacc[kb] = TT::mfma32x32x16(read_k_frag<TT>(lb, k_off[ks] + kb * 32 * kRowBytes),
-                                      qf[ks], sacc[kb]);
-      }
+        for (int kb = 0; kb < NKB; ++kb)
+          kf[kb][ks] = read_k_frag<TT>(lb, k_off[ks] + kb * 32 * kRowBytes);
+      f32x16 sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sacc[kb] = TT::mfma32x32x16(kf[kb][ks], qf[ks], sacc[kb]);
       const bool need_mask = krows < kBc || (s.causal && kpos0 + krows - 1 > wave_qlo);
       if (need_mask) {
         const int lim = visible_limit(krows, s.causal, q_pos - kpos0);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kk = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -208,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
       // online softmax with lazy rescaling (see fwd_mfma.hip)
       float mt = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
       mt = pair_max(mt);
@@ -223,9 +264,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
       }
       const float m_use = m_run == kNegInf ? 0.f : m_run;
       float rs = 0.f;
-      v8 pf[4];
+      v8 pf[NU];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = exp2_fast(fmaf(sacc[kb][r], p.c, -m_use));
@@ -235,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
       l_run += rs;
       // O^T += V^T P^T: MFMA u covers keys 16u .. 16u+15
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const uint32_t o = v_off[db] + 16 * u * kRowBytes;
@@ -290,11 +331,13 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
   const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq;
   if (blocks <= 0) return hipSuccess;
   if (out_f32)
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, true>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, true>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse,
+                       p, s);
   else
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, false>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, false>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse,
+                       p, s);
   return hipGetLastError();
 }
 

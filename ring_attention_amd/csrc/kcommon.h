@@ -121,6 +121,15 @@ __device__ __forceinline__ TileCursor cursor_begin(const Sched& s, int32_t rank,
   return c;
 }
 
+// Number of live key tiles of one query tile (what a cursor walks).
+template <int BC>
+__device__ __forceinline__ int64_t count_live_tiles(const Sched& s, int32_t rank, int64_t qhi) {
+  int64_t n = 0;
+  const int32_t nv = num_visits(s);
+  for (int32_t v = 0; v < nv; ++v) n += live_tiles(visit(s, rank, v), qhi, s.causal, BC);
+  return n;
+}
+
 template <int BC>
 __device__ __forceinline__ void cursor_next(TileCursor& c, const Sched& s, int32_t rank,
                                             int64_t qhi) {

@@ -62,6 +62,12 @@ int check_dtype_d(int dtype, int d) {
 
 bool use_mfma(int dtype, int d) { return dtype != RATTN_F32 && d >= 32; }
 
+// Query rows per tile of the kernel that will run (the schedule is built for it).
+int tile_rows(int dtype, int d) {
+  if (!use_mfma(dtype, d)) return kGenericBr;
+  return d == 128 ? kMfma128Br : kMfmaBr;
+}
+
 float resolve_scale(float scale, int d) {
   return (scale > 0.f && isfinite(scale)) ? scale : (float)(1.0 / sqrt((double)d));
 }
@@ -119,7 +125,7 @@ extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out,
   if (!tensor_ok(B, N, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
   if (Nq == 0) return RATTN_OK;
 
-  const int br = use_mfma(dtype, d) ? kMfmaBr : kGenericBr;
+  const int br = tile_rows(dtype, d);
   Sched s;
   memset(&s, 0, sizeof s);
   s.W = W;
@@ -178,7 +184,7 @@ extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_bl
   if (!tensor_ok(B, Nq > Nk ? Nq : Nk, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
   if (Nq == 0) return RATTN_OK;
 
-  const int br = use_mfma(dtype, d) ? kMfmaBr : kGenericBr;
+  const int br = tile_rows(dtype, d);
   Sched s;
   memset(&s, 0, sizeof s);
   s.mode = kVisitExplicit;
