@@ -1,34 +1,43 @@
-// fwd_mfma128.hip -- the d = 128 attention forward on gfx950 matrix cores.
+// fwd_mfma128.hip -- the d = 128 attention forward on gfx950 matrix cores,
+// two wave groups in ping-pong.
 //
-// Same method as fwd_mfma.hip (online softmax over key tiles with a running
-// max m, running sum l and unnormalised O, P rounded to the input type before
-// PV, O/l once at the end -- guijiagi.com "ring-attention-explained", online
+// Method (unchanged): online softmax over key tiles with a running max m,
+// running sum l and unnormalised O, P rounded to the input type before PV,
+// O/l once at the end (guijiagi.com "ring-attention-explained", online
 // softmax section; yz520gzy FlashAttention chapter, FlashAttention-2 and its
-// Triton kernel), with a data path built for head dimension 128:
+// Triton kernel).
 //
-//   * K and V tiles (64 keys x 128 dims, 16 KB each) move global -> LDS by
-//     direct-to-LDS DMA (global_load_lds_dwordx4): each wave instruction
-//     writes 1 KB = 4 rows, lane l to LDS byte 16*l of that block, so no
-//     registers stage the tile and no LDS store instructions are issued.
-//   * Each lane chooses which 16-byte chunk of its row it fetches, so rows
-//     are stored with their chunks XOR-swizzled: K chunk c of row r sits at
-//     slot c ^ (r % 16), V chunk c at slot c ^ 4*(r % 4).  Both tile reads
-//     below then touch every LDS bank equally (no bank conflicts).
-//   * S^T = K Q^T (v_mfma_f32_32x32x16): A = 16-byte K fragments (one
-//     ds_read_b128 each), B = the query tile held in registers.
-//   * O^T = V^T P^T: the V^T fragment (8 keys of one head dim per lane) comes
-//     from two ds_read_b64_tr_b16 transposing loads of the row-major V tile:
-//     in each group of 16 lanes, lane i receives element i%4 of the 8-byte
-//     pieces addressed by lanes 4k + i/4, k = 0..3; lanes address a 4-key x
-//     16-dim block so that lane i gets 4 consecutive keys of dim i.  The key
-//     order matches the P registers taken straight from the score
-//     accumulator (register r of lane l holds key 8(r/4) + 4(l/32) + r%4).
-//   * Tiles are double-buffered in two separate LDS arrays, and the tile loop
-//     is unrolled by two so that each step's buffers are known statically:
-//     the DMA of tile j+1 is issued before the matrix work of tile j, and
-//     the compiler can see that the reads of tile j do not touch the buffer
-//     the DMA is filling, so it waits for the DMA only at the one barrier
-//     per tile.
+// Schedule.  A workgroup of 8 wavefronts owns 256 query rows, 32 per wave;
+// waves w and w+4 share a SIMD.  Waves 0-3 form group A, waves 4-7 group B.
+// Per key tile k each group runs an MFMA phase M_k = {PV of tile k-1, QK of
+// tile k} (32 MFMAs) and a VALU phase V_k = {mask, max, exp, sum, P} of tile
+// k.  Group B runs one phase behind group A and a workgroup barrier ends
+// every phase ("slot"), so in each slot one group's softmax runs next to the
+// other group's matrix work on every SIMD:
+//      slot   0    1    2    3    4   ...
+//      A     M0   V0   M1   V1   M2
+//      B     --   M0   V0   M1   V1
+//
+// Every M phase runs the same 32-MFMA stream (a single code path keeps the
+// accumulators in place); a tile a wave does not score gets P = 0.  The
+// stream reads each MFMA's LDS operand a few MFMAs ahead.  Scalar
+// bookkeeping and DMA issue sit in the V phase, next to the VALU work.
+//
+// Data path.  K and V tiles (64 keys x 128 dims) move global -> LDS by
+// direct-to-LDS DMA into a ring of 4 buffers; tile k is requested three or
+// four slots before group A's QK reads it.  Rows
+// are stored with XOR-swizzled 16-byte chunks (K chunk c of row r at slot
+// c ^ (r%16), V at c ^ 4(r%4)) so the fragment reads below are conflict-free.
+// S^T = K Q^T with v_mfma_f32_32x32x16 (A = K fragment, B = Q held in
+// registers); O^T = V^T P^T with the V^T fragment from two ds_read_b64_tr_b16
+// transposing reads and P taken straight from the score registers (register
+// r of lane l holds key 8(r/4) + 4(l/32) + r%4 of a 32-key block).
+// The DMA is issued from inline assembly and waited for explicitly
+// (s_waitcnt vmcnt) before the barrier that precedes its first reader, so
+// the compiler adds no conservative waits between a DMA and unrelated LDS
+// reads.  Nothing else in this kernel uses M0.
+#include <type_traits>
+
 #include "kcommon.h"
 #include "launch.h"
 
@@ -37,63 +46,64 @@ namespace rattn {
 namespace {
 
 constexpr int D = 128;
-constexpr int kThreads = 256;  // 4 wavefronts x 32 query rows
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBr = 32 * kWaves;    // 256 query rows per workgroup
+constexpr int BC = 64;              // keys per tile
 constexpr int kRowBytes = D * 2;
+constexpr int kTileBytes = BC * kRowBytes;  // 16 KB
+constexpr int kBufBytes = 2 * kTileBytes;   // K + V
+constexpr int kNBuf = 4;
+constexpr int KS = D / 16;
+constexpr int DB = D / 32;
+constexpr int NKB = BC / 32;
+constexpr int NU = BC / 16;
+constexpr int kDmaBlocks = kBufBytes / 1024;          // 32 per tile
+constexpr int kDmaPerWave = kDmaBlocks / kWaves;      // 4 per wave per tile
 
-// Keys per tile: 64 (two resident workgroups per CU) or 32 (three).
-#ifndef RATTN_D128_BC
-#define RATTN_D128_BC 64
-#endif
-constexpr int BC = RATTN_D128_BC;
-static_assert(BC == 32 || BC == 64, "tile width");
-// A K+V buffer holds 2*BC rows of 256 bytes; each wave moves BC/16 1-KB DMA
-// blocks per tensor.
-constexpr int kTileBytes = BC * kRowBytes;
-constexpr int kBufBytes = 2 * kTileBytes;
-constexpr int NKB = BC / 32;   // 32-key score blocks
-constexpr int NU = BC / 16;    // 16-key PV steps
-constexpr int NDMA = BC / 16;  // DMA blocks per wave per tensor
-constexpr int kWavesPerEu = BC == 64 ? 2 : 3;
+static_assert(kBr == kMfma128Br, "schedule built for this tile height");
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ lds_void* lds_at(char* base, int byte_off) {
-  return (lds_void*)(base + byte_off);
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory");
 }
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_dma_but_one_tile() {
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // kDmaPerWave DMAs may stay in flight
+}
+__device__ __forceinline__ void slot_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <typename TT>
 __device__ __forceinline__ typename TT::v8 read_k_frag(const char* lds, uint32_t off) {
   return *(const typename TT::v8*)(lds + off);
 }
-
-// 4 consecutive keys of one head dim via the transposing LDS read.
 __device__ __forceinline__ v4s read_tr(const char* lds, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4s*)(
-          (__attribute__((address_space(3))) char*)(lds_void*)(lds + off)));
+          (__attribute__((address_space(3))) char*)(lds + off)));
 }
 
-static_assert(kThreads / 64 * 32 == kMfma128Br, "schedule built for this tile height");
-
 template <typename TT, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, kWavesPerEu) void fwd_mfma128_kernel(
+__global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
     FwdParams p, Sched s) {
   using E = typename TT::elem;
   using v8 = typename TT::v8;
   using v4 = typename TT::v4;
-  constexpr int KS = D / 16;  // 8 k-steps of S
-  constexpr int DB = D / 32;  // 4 row blocks of O^T
-  constexpr int kBc = BC;
+  using E2 = typename TT::v2;
 
-  __shared__ __attribute__((aligned(1024))) char smem0[kBufBytes];
-  __shared__ __attribute__((aligned(1024))) char smem1[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kBufBytes];
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;  // 0: A, 1: B (one phase behind)
   const int hl = lane >> 5;
   const int l32 = lane & 31;
   const int l16 = lane & 15;
@@ -114,7 +124,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerEu) void fwd_mfma128_kernel(
   const bool q_valid = my_q < qt.rows;
   const int64_t q_pos = qt.pos0 + my_q;
 
-  // ---- Q fragments (B operand), loaded once ------------------------------
   v8 qf[KS];
   {
     const E* qp = q + (((int64_t)b * p.Nq + qt.row0 + (q_valid ? my_q : 0)) * p.Hq + hq) * D +
@@ -132,171 +141,266 @@ __global__ __launch_bounds__(kThreads, kWavesPerEu) void fwd_mfma128_kernel(
   float m_run = kNegInf;
   float l_run = 0.f;
 
-  // ---- DMA addressing ----------------------------------------------------
-  const int64_t kv_stride = (int64_t)p.Hkv * D;  // elements between rows
+  // ---- DMA: wave w moves K blocks 2w, 2w+1 and V blocks 2w, 2w+1 ---------
+  const int64_t kv_stride = (int64_t)p.Hkv * D;
   const char* kbase = (const char*)(k + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D);
   const char* vbase = (const char*)(v + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D);
   const uint32_t row_bytes = (uint32_t)(kv_stride * sizeof(E));
-  // Tile rows handled by this wave: DMA blocks n = NDMA*wave + i,
-  // rows 4n + lane/16; lane l writes LDS slot l%16 of its row and fetches
-  // the logical chunk that belongs there.  Per-lane byte offsets from the
-  // tile's first row are fixed, so each DMA is one scalar tile base plus a
-  // 32-bit lane offset.
-  uint32_t kdma_off[NDMA], vdma_off[NDMA];
-  int dma_row[NDMA];
+  uint32_t kdma_off[2], vdma_off[2];
+  int dma_row[2];
 #pragma unroll
-  for (int i = 0; i < NDMA; ++i) {
-    const int r = 4 * (NDMA * wave + i) + (lane >> 4);
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * wave + i) + (lane >> 4);
     dma_row[i] = r;
     kdma_off[i] = (uint32_t)r * row_bytes + 16 * (l16 ^ (r & 15));
     vdma_off[i] = (uint32_t)r * row_bytes + 16 * (l16 ^ (4 * (r & 3)));
   }
-
-  auto issue_tile = [&](const TileCursor& c, char* lk) {
-    const int64_t krow0 = c.run.row0 + c.t * kBc;
-    const int64_t rem = c.run.len - c.t * kBc;
+  // This wave's four 16-byte-per-lane DMA parts of one tile: part 2i is K
+  // block 2w+i, part 2i+1 is V block 2w+i.
+  struct DmaPlan {
+    const char* src[4];
+    uint32_t dst[4];
+    bool on;
+  };
+  auto plan_tile = [&](const TileCursor& c, int buf) {
+    DmaPlan dp;
+    const int64_t krow0 = c.run.row0 + c.t * BC;
+    const int64_t rem = c.run.len - c.t * BC;
     const char* kt = kbase + krow0 * (int64_t)row_bytes;
     const char* vt = vbase + krow0 * (int64_t)row_bytes;
-    char* lv = lk + kTileBytes;
-    if (rem >= kBc) {
+    const uint32_t lk = smem_addr + buf * kBufBytes;
+    const uint32_t lv = lk + kTileBytes;
+    // ragged last tile of a run: rows past its end repeat the last row
+    // (finite values; their scores are masked, so p = 0 for them)
+    const int last = rem < BC ? (int)rem - 1 : BC - 1;
 #pragma unroll
-      for (int i = 0; i < NDMA; ++i) {
-        const int n = NDMA * wave + i;
-        __builtin_amdgcn_global_load_lds(kt + kdma_off[i], lds_at(lk, n * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + vdma_off[i], lds_at(lv, n * 1024), 16, 0, 0);
-      }
-    } else {
-      // ragged last tile of a run: rows past its end repeat the last row
-      // (finite values; their scores are masked, so p = 0 for them)
-      const uint32_t back_unit = row_bytes;
-      const int last = (int)rem - 1;
-#pragma unroll
-      for (int i = 0; i < NDMA; ++i) {
-        const int n = NDMA * wave + i;
-        const uint32_t back = dma_row[i] > last ? (uint32_t)(dma_row[i] - last) * back_unit : 0u;
-        __builtin_amdgcn_global_load_lds(kt + (kdma_off[i] - back), lds_at(lk, n * 1024), 16,
-                                         0, 0);
-        __builtin_amdgcn_global_load_lds(vt + (vdma_off[i] - back), lds_at(lv, n * 1024), 16,
-                                         0, 0);
-      }
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t back = dma_row[i] > last ? (uint32_t)(dma_row[i] - last) * row_bytes : 0u;
+      dp.src[2 * i] = kt + (kdma_off[i] - back);
+      dp.src[2 * i + 1] = vt + (vdma_off[i] - back);
+      dp.dst[2 * i] = lk + (2 * wave + i) * 1024;
+      dp.dst[2 * i + 1] = lv + (2 * wave + i) * 1024;
     }
+    dp.on = true;
+    return dp;
   };
 
-  // ---- fragment addressing: per-lane byte offsets inside one K+V buffer ----
-  // K: row kb*32 + l32, logical chunk 2*ks + hl at slot chunk ^ (row % 16)
+  // ---- fragment addressing inside one K+V buffer --------------------------
   uint32_t k_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     k_off[ks] = (uint32_t)(l32 * kRowBytes + 16 * ((2 * ks + hl) ^ (l32 & 15)));
-  // V (transposing read): lane i of 16-lane group g reads key row
-  // 16u + 8h + 4*hl + i/4, dims 32*db + 16*(g%2) + 4*(i%4) .. +3
   uint32_t v_off[DB];
   {
     const int qrow = l16 >> 2;
     const int g2 = (lane >> 4) & 1;
-    const int c_in = 2 * g2 + ((l16 & 3) >> 1);  // chunk within the 32-dim block
-    const int half = (l16 & 1) * 8;              // byte within the 16-byte chunk
+    const int c_in = 2 * g2 + ((l16 & 3) >> 1);
+    const int half = (l16 & 1) * 8;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
       v_off[db] = (uint32_t)(kTileBytes + (4 * hl + qrow) * kRowBytes +
                              16 * ((4 * db + c_in) ^ (4 * qrow)) + half);
   }
 
-  TileCursor cur = cursor_begin<kBc>(s, qt.rank, qhi);
-  if (cur.v < cur.nv) issue_tile(cur, smem0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // ---- tile bookkeeping ----------------------------------------------------
+  const int T = (int)count_live_tiles<BC>(s, qt.rank, qhi);  // tiles of this work item
+  TileCursor cdma = cursor_begin<BC>(s, qt.rank, qhi);        // next tile to request
+  TileCursor cqk = cdma;                                      // next tile this group scores
+  int n_req = 0;
+  // plan the next tile's DMA (none once all T tiles are requested)
+  auto plan_next = [&]() {
+    DmaPlan dp;
+    dp.on = false;
+    if (n_req < T) {
+      dp = plan_tile(cdma, n_req & (kNBuf - 1));
+      cursor_next<BC>(cdma, s, qt.rank, qhi);
+      ++n_req;
+    }
+    return dp;
+  };
+  auto issue_all = [&](const DmaPlan& dp) {
+    if (dp.on) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma16(dp.src[q], dp.dst[q]);
+    }
+  };
+  // Every M phase runs the full MFMA stream (one code path keeps the
+  // accumulators in place).  The first PV therefore reads the V half of
+  // buffer kNBuf-1 with P = 0: zero it so that 0 * V stays 0 (no DMA targets
+  // that buffer before both groups' first M phase).
+  {
+    uint4* z = (uint4*)(smem + (kNBuf - 1) * kBufBytes + kTileBytes);
+    for (int i = tid; i < kTileBytes / 16; i += kThreads) z[i] = uint4{0, 0, 0, 0};
+  }
+  issue_all(plan_next());  // tile 0
+  issue_all(plan_next());  // tile 1
+  if (T > 1) wait_dma_but_one_tile(); else wait_dma_all();
   __syncthreads();
 
-  auto step = [&](char* cur_buf, char* next_buf) {
-    TileCursor nxt = cur;
-    cursor_next<kBc>(nxt, s, qt.rank, qhi);
-    const bool has_next = nxt.v < nxt.nv;
-    if (has_next) issue_tile(nxt, next_buf);
-    const int64_t kpos0 = cur.run.pos0 + cur.t * kBc;
-    const int64_t rem = cur.run.len - cur.t * kBc;
-    const int krows = rem < kBc ? (int)rem : kBc;
-    const bool wave_sees = wave_active && (!s.causal || kpos0 <= wave_qhi);
-    if (wave_sees) {
-      const char* lb = cur_buf;
-      // S^T = K Q^T.  All K fragments of the tile are requested before the
-      // first MFMA so the LDS latency is paid once per tile, and the 32-key
-      // accumulator chains alternate.
-      v8 kf[NKB][KS];
+  // per-group state carried between phases
+  // sacc holds this wave's scores of the last scored tile; the V phase
+  // replaces them with P in the input type, packed into sacc[0] (key pair
+  // (r, r+1) of 32-key block kb -> dword 8 kb + r/2), which the next PV
+  // reads.  P = 0 when the wave did not score the tile.
+  f32x16 sacc[NKB];
+  static_assert(NKB == 2, "P of a 64-key tile fills exactly one accumulator");
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          kf[kb][ks] = read_k_frag<TT>(lb, k_off[ks] + kb * 32 * kRowBytes);
-      f32x16 sacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          sacc[kb] = TT::mfma32x32x16(kf[kb][ks], qf[ks], sacc[kb]);
-      const bool need_mask = krows < kBc || (s.causal && kpos0 + krows - 1 > wave_qlo);
-      if (need_mask) {
-        const int lim = visible_limit(krows, s.causal, q_pos - kpos0);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            sacc[kb][r] = kk < lim ? sacc[kb][r] : kNegInf;
-          }
+  for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+  int64_t s_kpos0 = 0;   // positions of the scored tile (for the mask)
+  int s_krows = 0;
+
+  // One M phase as a flat stream of MFMAs, PV first (16: u-major, db-minor,
+  // four independent accumulators), then QK (16: ks-major, kb-minor, two
+  // accumulators).  Each MFMA's LDS operand is read kAhead MFMAs before it
+  // is used, so the reads stream under the matrix work of the same wave.
+  constexpr int kAhead = 4;
+  auto mfma_stream = [&](auto pv_tag, auto qk_tag, const char* pvb, const char* qkb) {
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr int NPV = PV ? NU * DB : 0;
+    constexpr int N = NPV + (QK ? KS * NKB : 0);
+    auto load = [&](int i) -> v8 {
+      if (PV && i < NPV) {
+        const uint32_t o = v_off[i % DB] + 16 * (i / DB) * kRowBytes;
+        const v4s lo = read_tr(pvb, o);
+        const v4s hi = read_tr(pvb, o + 8 * kRowBytes);
+        return __builtin_shufflevector(__builtin_bit_cast(v4, lo), __builtin_bit_cast(v4, hi), 0,
+                                       1, 2, 3, 4, 5, 6, 7);
       }
-      // online softmax with lazy rescaling (see fwd_mfma.hip)
-      float mt = kNegInf;
+      const int j = i - NPV;
+      return read_k_frag<TT>(qkb, k_off[j / NKB] + (j % NKB) * 32 * kRowBytes);
+    };
+    v8 fb[kAhead];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int i = 0; i < kAhead; ++i)
+      if (i < N) fb[i] = load(i);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      mt = pair_max(mt);
-      const float m_cand = mt * p.c;
-      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, m_cand);
-        const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    for (int i = 0; i < N; ++i) {
+      const v8 a = fb[i % kAhead];
+      if (i + kAhead < N) fb[i % kAhead] = load(i + kAhead);
+      if (PV && i < NPV) {
+        const int u = i / DB;
+        const f32x4 pw = {sacc[0][4 * u], sacc[0][4 * u + 1], sacc[0][4 * u + 2],
+                          sacc[0][4 * u + 3]};
+        oacc[i % DB] = TT::mfma32x32x16(a, __builtin_bit_cast(v8, pw), oacc[i % DB]);
+      } else {
+        const int j = i - NPV;
+        sacc[j % NKB] = TT::mfma32x32x16(a, qf[j / NKB], j < NKB ? f32x16{} : sacc[j % NKB]);
       }
-      const float m_use = m_run == kNegInf ? 0.f : m_run;
-      float rs = 0.f;
-      v8 pf[NU];
+      __builtin_amdgcn_sched_barrier(0);  // keep this issue order
+    }
+  };
+
+  // M phase kk: PV of tile kk-1 (P = 0 for kk = 0 or a tile this wave did
+  // not score), then QK of tile kk (its scores are unused for kk = T).
+  // The DMA of tile kk+2 (if any) is issued first.  The wave runs this
+  // phase at raised priority, so that on its SIMD the issue arbiter prefers
+  // its MFMAs over the partner wave's softmax VALU (oldest-first would favour
+  // group A in both phases).
+  auto m_phase = [&](int kk) {
+    using yes = std::integral_constant<bool, true>;
+    const char* pvb = smem + ((kk - 1) & (kNBuf - 1)) * kBufBytes;
+    const char* qkb = smem + (kk & (kNBuf - 1)) * kBufBytes;
+    __builtin_amdgcn_s_setprio(1);
+    issue_all(plan_next());
+    mfma_stream(yes{}, yes{}, pvb, qkb);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // V phase: mask, running max (lazy rescale), exp, row sum, P of the tile
+  // scored in the last M phase.
+  // The scalar bookkeeping (tile positions, cursor) runs here too, where it
+  // issues between the VALU work instead of delaying the matrix stream.
+  auto v_phase = [&]() {
+    s_kpos0 = cqk.run.pos0 + cqk.t * BC;
+    const int64_t rem = cqk.run.len - cqk.t * BC;
+    s_krows = rem < BC ? (int)rem : BC;
+    const bool s_live = wave_active && (!s.causal || s_kpos0 <= wave_qhi);
+    cursor_next<BC>(cqk, s, qt.rank, qhi);
+    if (!s_live) {
+      sacc[0] = f32x16{};  // P = 0
+      return;
+    }
+    const bool need_mask = s_krows < BC || (s.causal && s_kpos0 + s_krows - 1 > wave_qlo);
+    if (need_mask) {
+      // key index of register r of block kb is kb*32 + 8(r/4) + 4hl + r%4;
+      // compare its lane-independent part against the limit shifted by 4hl
+      const int lim = visible_limit(s_krows, s.causal, q_pos - s_kpos0) - 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pr = exp2_fast(fmaf(sacc[kb][r], p.c, -m_use));
-          rs += pr;
-          pf[2 * kb + (r >> 3)][r & 7] = to_elem<TT>(pr);
-        }
-      l_run += rs;
-      // O^T += V^T P^T: MFMA u covers keys 16u .. 16u+15
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint32_t o = v_off[db] + 16 * u * kRowBytes;
-          const v4s lo = read_tr(lb, o);
-          const v4s hi = read_tr(lb, o + 8 * kRowBytes);
-          const v8 a = __builtin_shufflevector(__builtin_bit_cast(v4, lo),
-                                               __builtin_bit_cast(v4, hi), 0, 1, 2, 3, 4, 5,
-                                               6, 7);
-          oacc[db] = TT::mfma32x32x16(a, pf[u], oacc[db]);
+          const int kk2 = kb * 32 + 8 * (r >> 2) + (r & 3);
+          sacc[kb][r] = kk2 < lim ? sacc[kb][r] : kNegInf;
         }
     }
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    cur = nxt;
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+    mt = pair_max(mt);
+    const float m_cand = mt * p.c;
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    // l sums P in fp32 (before rounding), four partial sums
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_fast(fmaf(sacc[kb][r], p.c, -m_use));
+        const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], p.c, -m_use));
+        rs[(r >> 1) & 3] += p0;
+        rs[(r >> 1) & 3] += p1;
+        const E2 pair = {to_elem<TT>(p0), to_elem<TT>(p1)};
+        sacc[0][8 * kb + r / 2] = __builtin_bit_cast(float, pair);
+      }
+    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
-  while (cur.v < cur.nv) {
-    step(smem0, smem1);
-    if (!(cur.v < cur.nv)) break;
-    step(smem1, smem0);
+
+  // Before group A's QK of tile j (even slot 2j) tile j must have landed on
+  // every wave; only tile j+1's requests may still be in flight.
+  auto wait_tile = [&](int j) {
+    if (j + 1 < T) wait_dma_but_one_tile(); else wait_dma_all();
+  };
+
+  // DMA: each wave requests its share of tile m at the start of its M phase
+  // for tile m-2, group A in slot 2m-4, group B in slot 2m-3.  Buffer m%4
+  // last held tile m-4, whose last reader (group B's PV) ran in slot 2m-5.
+  // Every wave waits for tile m at the end of slot 2m-1, before group A's QK
+  // reads it; only tile m+1's requests may still be in flight then.  The
+  // DMA issue (scalar and memory instructions) fits between the MFMAs.
+  // Both groups pass 2T+2 barriers.
+  if (group == 0) {
+    for (int j = 0; j < T; ++j) {
+      m_phase(j);      // slot 2j (requests tile j+2)
+      slot_barrier();
+      v_phase();       // slot 2j+1
+      wait_tile(j + 1);
+      slot_barrier();
+    }
+    m_phase(T);        // slot 2T: PV of the last tile
+    slot_barrier();
+    slot_barrier();    // slot 2T+1
+  } else {
+    slot_barrier();    // slot 0
+    for (int j = 0; j < T; ++j) {
+      m_phase(j);      // slot 2j+1 (requests tile j+2)
+      wait_tile(j + 1);
+      slot_barrier();
+      v_phase();       // slot 2j+2
+      slot_barrier();
+    }
+    m_phase(T);        // slot 2T+1
+    slot_barrier();
   }
   // ---- epilogue: O / l, LSE = m ln2 + ln l --------------------------------
   const float l_tot = pair_sum(l_run);
@@ -331,13 +435,11 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
   const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq;
   if (blocks <= 0) return hipSuccess;
   if (out_f32)
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, true>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse,
-                       p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, true>), dim3((unsigned)blocks), dim3(kThreads),
+                       0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse, p, s);
   else
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, false>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse,
-                       p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, false>), dim3((unsigned)blocks), dim3(kThreads),
+                       0, stream, (const E*)q, (const E*)k, (const E*)v, out, lse, p, s);
   return hipGetLastError();
 }
 

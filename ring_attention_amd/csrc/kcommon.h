@@ -27,6 +27,7 @@ struct Bf16 {
   typedef __bf16 elem;
   typedef __bf16 v8 __attribute__((ext_vector_type(8)));
   typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -35,6 +36,7 @@ struct F16 {
   typedef _Float16 elem;
   typedef _Float16 v8 __attribute__((ext_vector_type(8)));
   typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }

@@ -9,7 +9,7 @@ namespace rattn {
 // Query rows per tile of each forward kernel; the schedule is built for it.
 constexpr int kGenericBr = 64;
 constexpr int kMfmaBr = 128;     // fwd_mfma (16-bit, d = 32, 64)
-constexpr int kMfma128Br = 128;  // fwd_mfma128 (16-bit, d = 128)
+constexpr int kMfma128Br = 256;  // fwd_mfma128 (16-bit, d = 128)
 
 hipError_t launch_fwd_generic(int dtype, int d, const void* q, const void* k, const void* v,
                               void* out, float* lse, bool out_f32, const FwdParams& p,
