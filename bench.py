@@ -22,6 +22,8 @@ the same way (extras).
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +36,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, true>"  # d=128 16-bit path, fp32 partials
+# sources the step kernel is built from; the stored counter summary is valid
+# only for the kernel it was measured on
+KERNEL_SOURCES = ("fwd_mfma128.hip", "kcommon.h", "ring_sched.h", "launch.h")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles",
+                               "fwd_mfma128_zigzag_rank2_131k_bf16_hbm_counters.txt")
 METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 MI355X"
 
 
@@ -49,7 +57,87 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose byte "
                          "counters calibrate the kernels' FETCH_SIZE/WRITE_SIZE readings")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                    help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, then WRITE_SIZE; counter_collection.csv) and exit")
     return ap.parse_args()
+
+
+# ------------------------------------------------------------ profile summaries
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ring_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def summarize_stats(path: str) -> None:
+    """Top kernels of a rocprofv3 --stats run: calls, average and total time."""
+    rows = list(csv.DictReader(open(path)))
+    print(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+    for r in rows[:12]:
+        print(f"{_short_name(r['Name'])[:60]:60s} {int(r['Calls']):6d} "
+              f"{float(r['AverageNs']) / 1e3:10.1f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+              f"{float(r['Percentage']):6.2f}")
+
+
+def _counter_means(path: str, counter: str):
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(_short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_counters(fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per launch of the step kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the 1 GiB copy of
+    --copy-probe (the largest copy dispatch in the run)."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    copy_f = max(v for n, vs in fetch.items() if "copy" in n for v in vs)
+    copy_w = max(v for n, vs in write.items() if "copy" in n for v in vs)
+    f_scale, w_scale = gib_kib / copy_f, gib_kib / copy_w
+    kf, kw = fetch[STEP_KERNEL], write[STEP_KERNEL]
+    fetch_b = sum(kf) / len(kf) * 1024 * f_scale
+    write_b = sum(kw) / len(kw) * 1024 * w_scale
+    print(f"kernel: {STEP_KERNEL}")
+    print(f"kernel_source_sha256_16: {kernel_source_hash()}")
+    print(f"copy_probe_fetch_kib: {copy_f:.0f}  (1 GiB copy; scale {f_scale:.4f})")
+    print(f"copy_probe_write_kib: {copy_w:.0f}  (1 GiB copy; scale {w_scale:.4f})")
+    print(f"step_kernel_dispatches: {len(kf)} {len(kw)}")
+    print(f"step_kernel_fetch_kib_avg: {sum(kf) / len(kf):.1f}")
+    print(f"step_kernel_write_kib_avg: {sum(kw) / len(kw):.1f}")
+    print(f"step_kernel_hbm_read_bytes_per_launch: {fetch_b:.0f}")
+    print(f"step_kernel_hbm_write_bytes_per_launch: {write_b:.0f}")
+    print(f"step_kernel_hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
+
+
+def stored_traffic():
+    """HBM bytes per step-kernel launch from the committed counter summary, or None
+    when it is missing or was measured on other kernel sources."""
+    try:
+        kv = {}
+        for line in open(COUNTER_SUMMARY):
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.split()[0] if val.split() else ""
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return int(kv["step_kernel_hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------- pair counts
@@ -108,9 +196,15 @@ def step_plan(N, W, rank, c):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see DESIGN.md on sharding)", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
 
     import torch
 
@@ -206,7 +300,7 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "fwd_mfma_kernel<Bf16,128,out_f32>",
+                     "traffic": stored_traffic(), "kernel": STEP_KERNEL,
                      "avg_launch_ms": round(kern_ms, 4), "launches": n_launch},
         "merge_avg_ms": round(merge_ms, 4),
         "fused": {"value": round(fused_value, 2), "ms": round(fused_ms, 4),
