@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, then WRITE_SIZE; counter_collection.csv) and exit")
+    ap.add_argument("--summarize-mfma", metavar="SQ_CSV",
+                    help="print MFMA / VALU / LDS utilisation of the step kernel from a "
+                         "rocprofv3 --pmc run of the SQ counters and GRBM_GUI_ACTIVE and exit")
     return ap.parse_args()
 
 
@@ -122,6 +125,36 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     print(f"step_kernel_hbm_read_bytes_per_launch: {fetch_b:.0f}")
     print(f"step_kernel_hbm_write_bytes_per_launch: {write_b:.0f}")
     print(f"step_kernel_hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
+
+
+def summarize_mfma(path: str) -> None:
+    """Matrix-core utilisation of the step kernel: SQ_VALU_MFMA_BUSY_CYCLES over
+    the SIMD-cycles of the dispatch (GRBM_GUI_ACTIVE is summed over the 8 XCDs,
+    each with 32 CUs x 4 SIMDs), plus instruction counts per dispatch."""
+    per, dur = {}, {}
+    for r in csv.DictReader(open(path)):
+        if _short_name(r["Kernel_Name"]) != STEP_KERNEL:
+            continue
+        key = r["Dispatch_Id"]
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    n = len(per)
+    avg = {c: sum(d[c] for d in per.values()) / n for c in next(iter(per.values()))}
+    t = sum(dur.values()) / n
+    xcd_cycles = avg["GRBM_GUI_ACTIVE"] / 8
+    simd_cycles = xcd_cycles * 8 * 32 * 4
+    print(f"kernel: {STEP_KERNEL}")
+    print(f"kernel_source_sha256_16: {kernel_source_hash()}")
+    print(f"dispatches: {n}")
+    print(f"avg_duration_us: {t * 1e6:.1f}")
+    print(f"clock_ghz_from_grbm: {xcd_cycles / t / 1e9:.3f}")
+    print(f"mfma_busy_fraction: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.4f}")
+    print(f"mfma_issued_tflops: {avg['SQ_INSTS_MFMA'] * 32768 / t / 1e12:.1f}"
+          "  (every v_mfma_f32_32x32x16 counted as 32768 FLOP, masked work included)")
+    print(f"valu_active_fraction: {avg['SQ_ACTIVE_INST_VALU'] / simd_cycles:.4f}")
+    print(f"lds_bank_conflict_cycles: {avg['SQ_LDS_BANK_CONFLICT']:.0f}")
+    for c in sorted(avg):
+        print(f"  {c}: {avg[c]:.6g}")
 
 
 def stored_traffic():
@@ -204,6 +237,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
 
     import torch

@@ -309,6 +309,46 @@ def test_step_two_key_segments(gpu):
     compare(host(out), host(lse), ref_o, ref_l, torch.float16, what="step, two key runs")
 
 
+# The d = 128 16-bit kernel works on 256-row query tiles (8 waves of 32
+# rows) and 64-key tiles; these cases cross several of both, end on ragged
+# tails (inactive waves, partial key tiles) and put the causal diagonal off
+# every tile boundary.
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_several_query_and_key_tiles_ragged(gpu, dtype, causal):
+    N = 2 * 256 + 37  # three query tiles, the last with 37 rows; 8 key tiles + 37
+    q, k, v = workloads.make_qkv(1, N, N, 4, 2, 128, dtype, seed=41 + causal)
+    run_full_check(q, k, v, causal, 1, False, -1, f"d=128 N={N} {dtype} causal={causal}")
+
+
+def test_d128_step_offset_diagonal(gpu):
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_qkv(1, 300, 400, 2, 2, 128, torch.bfloat16, seed=43)
+    q_segs, k_segs = [(100, 300)], [(0, 400)]
+    out, lse = binding.fwd_step(q.to(dev), k.to(dev), v.to(dev), True, q_segs, k_segs)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(q, k, v, causal=True, q_pos=np.arange(100, 400),
+                                    k_pos=np.arange(0, 400))
+    compare(host(out), host(lse), ref_o, ref_l, torch.bfloat16, what="d=128 step, diagonal")
+
+
+def test_d128_step_query_tiles_without_keys(gpu):
+    dev = torch.device("cuda:0")
+    q, k, v = workloads.make_qkv(1, 600, 200, 2, 1, 128, torch.float16, seed=47)
+    # 300 queries before every key (whole 256-row tiles with no live key tile),
+    # then 300 queries after them
+    q_segs, k_segs = [(0, 300), (5000, 300)], [(1000, 200)]
+    out, lse = binding.fwd_step(q.to(dev), k.to(dev), v.to(dev), True, q_segs, k_segs)
+    torch.cuda.synchronize()
+    qpos = np.concatenate([np.arange(0, 300), np.arange(5000, 5300)])
+    ref_o, ref_l = oracle.attention(q, k, v, causal=True, q_pos=qpos,
+                                    k_pos=np.arange(1000, 1200))
+    compare(host(out), host(lse), ref_o, ref_l, torch.float16, what="d=128 step, no keys")
+    assert np.isneginf(host(lse)[0, :300]).all() and (host(out)[0, :300] == 0).all()
+
+
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 def test_merge_kernel(gpu, d):
     dev = torch.device("cuda:0")
