@@ -57,11 +57,17 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose byte "
                          "counters calibrate the kernels' FETCH_SIZE/WRITE_SIZE readings")
+    ap.add_argument("--small-d-only", action="store_true",
+                    help="run only the small head-dim sweep (after --copy-probe, if given) "
+                         "and print its JSON")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, then WRITE_SIZE; counter_collection.csv) and exit")
+    ap.add_argument("--summarize-kernels", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "SQ_CSV"),
+                    help="print per-kernel HBM GB/s and MFMA busy from three rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE, SQ counters) and exit")
     ap.add_argument("--summarize-mfma", metavar="SQ_CSV",
                     help="print MFMA / VALU / LDS utilisation of the step kernel from a "
                          "rocprofv3 --pmc run of the SQ counters and GRBM_GUI_ACTIVE and exit")
@@ -157,6 +163,41 @@ def summarize_mfma(path: str) -> None:
         print(f"  {c}: {avg[c]:.6g}")
 
 
+def summarize_kernels(fetch_csv: str, write_csv: str, sq_csv: str) -> None:
+    """Per kernel instantiation of this library: dispatches, average duration,
+    HBM bytes per dispatch (FETCH_SIZE + WRITE_SIZE, each scaled by the 1 GiB
+    copy of --copy-probe in its run), achieved HBM GB/s, and the matrix-core
+    busy fraction and VALU instructions from an SQ counter pass."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    f_scale = float(1 << 20) / max(v for n, vs in fetch.items() if "copy" in n for v in vs)
+    w_scale = float(1 << 20) / max(v for n, vs in write.items() if "copy" in n for v in vs)
+    per, dur = {}, {}
+    for r in csv.DictReader(open(sq_csv)):
+        name = _short_name(r["Kernel_Name"])
+        if not name.startswith("rattn::"):
+            continue
+        per.setdefault(name, {}).setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = \
+            float(r["Counter_Value"])
+        dur.setdefault(name, {})[r["Dispatch_Id"]] = \
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    print(f"{'kernel':46s} {'n':>4s} {'avg_us':>9s} {'HBM_MB':>8s} {'GB/s':>8s} "
+          f"{'mfma_busy':>9s} {'valu_instr/disp':>15s}")
+    for name in sorted(per):
+        d = per[name]
+        n = len(d)
+        t = sum(dur[name].values()) / n
+        avg = {c: sum(x.get(c, 0.0) for x in d.values()) / n for c in next(iter(d.values()))}
+        simd_cycles = avg["GRBM_GUI_ACTIVE"] / 8 * 1024
+        hbm = None
+        if name in fetch and name in write:
+            hbm = (sum(fetch[name]) / len(fetch[name]) * f_scale +
+                   sum(write[name]) / len(write[name]) * w_scale) * 1024
+        print(f"{name[:46]:46s} {n:4d} {t * 1e6:9.1f} "
+              f"{(hbm or 0) / 1e6:8.1f} {(hbm or 0) / t / 1e9:8.1f} "
+              f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:9.4f} {avg['SQ_INSTS_VALU']:15.4g}")
+
+
 def stored_traffic():
     """HBM bytes per step-kernel launch from the committed counter summary, or None
     when it is missing or was measured on other kernel sources."""
@@ -241,6 +282,9 @@ def main():
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
         return
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels)
+        return
 
     import torch
 
@@ -258,6 +302,10 @@ def main():
         dst.copy_(src)  # reads exactly 1 GiB, writes exactly 1 GiB
         torch.cuda.synchronize()
         del src, dst
+    if args.small_d_only:
+        print(json.dumps({"extras": small_d_sweep(torch, binding, workloads, dev, args)}),
+              flush=True)
+        return
     w = workloads.workload(4)
     W, rank, N, d, Hq = w.W, w.rank, w.N, w.d, w.Hq
     c = N // (2 * W)
@@ -290,6 +338,13 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
     value = flop_per_step / (ms_per_step * 1e-3) / 1e12
+
+    # the same steps timed one by one (median and minimum)
+    per_step = Timer(torch)
+    for _ in range(args.steps):
+        per_step(one_step)
+    per_step.total_ms()
+    step_ms = sorted(a.elapsed_time(b) for a, b in per_step.pairs)
 
     # per-launch timing of the dominant kernel (the step kernel), on the same stream
     kern = Timer(torch)
@@ -324,6 +379,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -332,7 +389,10 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "N": N, "Hq": Hq, "Hkv": w.Hkv,
                    "d": d, "causal": True, "ring": W, "zigzag": True, "rank": rank,
                    "mode": "8 ring-step launches + 7 LSE merges",
-                   "visible_pairs_per_head": pairs},
+                   "visible_pairs_per_head": pairs,
+                   "flop_per_step": flop_per_step,
+                   # the usual causal estimate, half of all (query, key) pairs
+                   "conventional_flop_per_step": 4 * d * Hq * w.B * w.Nq * N // 2},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -369,12 +429,39 @@ def main():
                                                     / PEAK_BF16_TFLOPS, 2)}
             del qe, ke, ve
             torch.cuda.empty_cache()
+        extras.update(small_d_sweep(torch, binding, workloads, dev, args))
         result["extras"] = extras
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
 
     print(json.dumps(result), flush=True)
+
+
+def small_d_sweep(torch, binding, workloads, dev, args):
+    """Small head dims at the batched causal shape (B=2, 4096 tokens, 32 heads,
+    fp16). Compulsory HBM bytes = q, k, v read + out written (input dtype) +
+    lse written (fp32)."""
+    out = {}
+    w3 = workloads.workload(3)
+    pe = causal_pairs(np.arange(w3.N), np.arange(w3.N))
+    for dd in (16, 32, 64):
+        qe, ke, ve = workloads.make_qkv(w3.B, w3.N, w3.N, w3.Hq, w3.Hkv, dd, torch.float16,
+                                        seed=3, device=dev)
+        fe = 4 * dd * w3.Hq * w3.B * pe
+        comp = (qe.numel() + ke.numel() + ve.numel() + qe.numel()) * 2 + qe.numel() // dd * 4
+        for _ in range(args.warmup):
+            binding.fwd(qe, ke, ve, causal=True)
+        te = Timer(torch)
+        for _ in range(args.steps):
+            te(lambda: binding.fwd(qe, ke, ve, causal=True))
+        ms = te.total_ms() / args.steps
+        out[f"mha_causal_b2_h32_4k_d{dd}_f16"] = {
+            "ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
+            "compulsory_bytes": comp, "compulsory_GBps": round(comp / (ms * 1e-3) / 1e9, 1)}
+        del qe, ke, ve
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, q, k, v, n_rows):
@@ -393,10 +480,21 @@ def cpu_baseline(w, q, k, v, n_rows):
     dt = time.perf_counter() - t
     pairs = int((qpos[rows[:, 1]] + 1).sum())  # keys 0..N-1, natural order
     flop = 4 * w.d * pairs
+    all_pairs = int((qpos + 1).sum()) * w.Hq * w.B
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_rows} seeded (row, head) query rows of the same workload, "
-                      f"{pairs} visible pairs, {dt:.2f} s wall"}
+                      f"{pairs} visible pairs, {dt:.2f} s wall",
+            "rows_per_s": round(n_rows / dt, 1),
+            "full_workload_s_extrapolated": round(dt * all_pairs / pairs, 1),
+            "cpu_model": model, "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":
