@@ -427,6 +427,25 @@ def main():
             extras[we.name] = {"ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
                                "pct_of_peak": round(100 * fe / (ms * 1e-3) / 1e12
                                                     / PEAK_BF16_TFLOPS, 2)}
+            ns = binding.split_hint(qe, ke, we.W, we.zigzag, we.rank)
+            if ns > 1:  # too few query tiles for the GPU: the split-KV entry point
+                ws = torch.empty(ns * qe.numel() // we.d * (we.d + 1), dtype=torch.float32,
+                                 device=dev)
+
+                def run_split():
+                    return binding.fwd_split(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
+                                             zigzag=we.zigzag, rank=we.rank, n_splits=ns, ws=ws)
+                for _ in range(args.warmup):
+                    run_split()
+                te = Timer(torch)
+                for _ in range(reps):
+                    te(run_split)
+                ms = te.total_ms() / reps
+                extras[we.name + "_splitkv"] = {
+                    "ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
+                    "pct_of_peak": round(100 * fe / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                    "n_splits": ns}
+                del ws
             del qe, ke, ve
             torch.cuda.empty_cache()
         extras.update(small_d_sweep(torch, binding, workloads, dev, args))

@@ -111,6 +111,34 @@ RATTN_API int rattn_merge(float* out, float* lse, const float* blk_out, const fl
                 int B, int H, int64_t Nq, int64_t Nb, int64_t row_off, int d,
                 void* stream);
 
+/*
+ * rattn_fwd with split-KV: the same schedule and result, with the live
+ * key/value tiles of every query tile divided into n_splits contiguous
+ * ranges, each processed by its own workgroup, and the n_splits partial
+ * results combined by the n-way form of the log-sum-exp merge (Twinkle page,
+ * update_out_and_lse, applied n_splits - 1 times).  For shapes whose query
+ * tiles alone cannot fill the GPU (few heads, short sequences).
+ * ws: caller-owned DEVICE scratch of ws_floats float32 elements, at least
+ * n_splits * B * Nq * Hq * (d + 1), 16-byte aligned, not overlapping the
+ * other tensors; the call overwrites it.  1 <= n_splits <= 64; n_splits = 1
+ * is rattn_fwd (ws unused).  Other arguments and errors as rattn_fwd;
+ * RATTN_EINVAL also when ws is null or too small.
+ */
+RATTN_API int rattn_fwd_split(const void* q, const void* k, const void* v, void* out,
+                              float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d,
+                              int dtype, float scale, int causal, int n_ring_steps, int zigzag,
+                              int rank, int n_splits, float* ws, int64_t ws_floats,
+                              void* stream);
+
+/*
+ * A split count for rattn_fwd_split: 1 when the query tiles alone give at
+ * least one workgroup per two compute units (n_cu compute units), else
+ * enough splits to reach that, keeping at least eight 64-key tiles per split
+ * and at most 64 splits.  Returns 1 for arguments rattn_fwd would reject.
+ */
+RATTN_API int rattn_split_hint(int B, int Hq, int64_t Nq, int64_t N, int d, int dtype,
+                               int n_ring_steps, int zigzag, int rank, int n_cu);
+
 /* Static description of a status code; never NULL. */
 RATTN_API const char* rattn_status_string(int status);
 

@@ -20,7 +20,8 @@ RATTN_OK, RATTN_EINVAL, RATTN_EUNSUPPORTED, RATTN_EHIP = 0, -1, -2, -3
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # Exported symbols, in the order include/rattn.h declares them.
-EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_merge", "rattn_status_string")
+EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_merge", "rattn_fwd_split", "rattn_split_hint",
+           "rattn_status_string")
 
 
 class RattnError(RuntimeError):
@@ -53,6 +54,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                    i32, i64p, i64p, i64p, i64p, vp]
     lib.rattn_merge.restype = i32
     lib.rattn_merge.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp]
+    lib.rattn_fwd_split.restype = i32
+    lib.rattn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
+                                    i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.rattn_split_hint.restype = i32
+    lib.rattn_split_hint.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32]
     lib.rattn_status_string.restype = ctypes.c_char_p
     lib.rattn_status_string.argtypes = [i32]
     if path is None:
@@ -116,6 +122,46 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                        int(bool(causal)), int(n_ring_steps), int(bool(zigzag)), int(rank),
                        _stream(q))
     _check("rattn_fwd", rc)
+    return out, lse
+
+
+def split_hint(q: torch.Tensor, k: torch.Tensor, n_ring_steps: int = 1, zigzag: bool = False,
+               rank: int = -1) -> int:
+    """rattn_split_hint for these shapes on q's device."""
+    B, Nq, Hq, d = q.shape
+    n_cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+    return int(load_library().rattn_split_hint(B, Hq, Nq, k.shape[1], d, DTYPE_CODES[q.dtype],
+                                               int(n_ring_steps), int(bool(zigzag)), int(rank),
+                                               n_cu))
+
+
+def fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+              n_ring_steps: int = 1, zigzag: bool = False, rank: int = -1,
+              scale: float | None = None, n_splits: int | None = None,
+              out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None):
+    """rattn_fwd with split-KV (rattn_fwd_split); n_splits=None takes
+    rattn_split_hint's count.  The float32 scratch is allocated here unless
+    given.  Same result as fwd()."""
+    _qkv(q, k, v)
+    B, Nq, Hq, d = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    if n_splits is None:
+        n_splits = split_hint(q, k, n_ring_steps, zigzag, rank)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    need = n_splits * B * Nq * Hq * (d + 1) if n_splits > 1 else 0
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    rc = lib.rattn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, Hq, Hkv, Nq, N, d, DTYPE_CODES[q.dtype],
+                             _scale(scale), int(bool(causal)), int(n_ring_steps),
+                             int(bool(zigzag)), int(rank), int(n_splits), ws.data_ptr(),
+                             ws.numel(), _stream(q))
+    _check("rattn_fwd_split", rc)
     return out, lse
 
 

@@ -30,8 +30,9 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(
 
   const int lane = threadIdx.x;
   const int32_t BH = p.B * p.Hq;
-  const int32_t bh = blockIdx.x % BH;
-  const int32_t t_lin = blockIdx.x / BH;
+  const WorkItem wi = work_item(BH, p.n_splits);
+  const int32_t bh = wi.bh;
+  const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
   const QTile qt = query_tile(s, t_lin);
 
@@ -49,8 +50,9 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(
   }
   float m = kNegInf, l = 0.f;
 
-  TileCursor cur = cursor_begin<BC>(s, qt.rank, qhi);
-  while (cur.v < cur.nv) {
+  int64_t left;  // key tiles of this split still to visit
+  TileCursor cur = split_cursor<BC>(s, qt.rank, qhi, wi.split, p.n_splits, &left);
+  for (; left > 0; --left) {
     const int64_t krow0 = cur.run.row0 + cur.t * BC;
     const int64_t kpos0 = cur.run.pos0 + cur.t * BC;
     const int64_t rem = cur.run.len - cur.t * BC;
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(
   const float inv = seen ? 1.f / l : 0.f;
   const int64_t o_off = (((int64_t)b * p.Nq + qt.row0 + lane) * p.Hq + hq) * D;
   if (OUT_F32) {
-    float* o = (float*)out + o_off;
+    float* o = (float*)out + wi.split * p.split_out_stride + o_off;
 #pragma unroll
     for (int t = 0; t < D; ++t) o[t] = acc[t] * inv;
   } else {
@@ -114,7 +116,8 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(
 #pragma unroll
     for (int t = 0; t < D; ++t) o[t] = to_elem<TT>(acc[t] * inv);
   }
-  lse[((int64_t)b * p.Nq + qt.row0 + lane) * p.Hq + hq] = seen ? m * kLn2 + logf(l) : kNegInf;
+  lse[wi.split * p.split_lse_stride + ((int64_t)b * p.Nq + qt.row0 + lane) * p.Hq + hq] =
+      seen ? m * kLn2 + logf(l) : kNegInf;
 }
 
 // Host-side launchers (declared in launch.h).
@@ -123,7 +126,7 @@ static hipError_t launch_generic_t(const void* q, const void* k, const void* v, 
                                    float* lse, bool out_f32, const FwdParams& p,
                                    const Sched& s, hipStream_t stream) {
   using E = typename TT::elem;
-  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq;
+  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq * p.n_splits;
   if (blocks <= 0) return hipSuccess;
   if (out_f32)
     hipLaunchKernelGGL((fwd_generic_kernel<TT, D, true>), dim3((unsigned)blocks), dim3(64), 0,

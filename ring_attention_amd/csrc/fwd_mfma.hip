@@ -75,8 +75,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
 
   // ---- work item -------------------------------------------------------
   const int32_t BH = p.B * p.Hq;
-  const int32_t bh = xcd_head_swizzle((int32_t)(blockIdx.x % BH), BH);
-  const int32_t t_lin = blockIdx.x / BH;
+  const WorkItem wi = work_item(BH, p.n_splits);
+  const int32_t bh = xcd_head_swizzle(wi.bh, BH);
+  const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
   const QTile qt = query_tile(s, t_lin);
   const int64_t qhi = qt.pos0 + qt.rows - 1;
@@ -177,16 +178,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
     }
   };
 
-  TileCursor cur = cursor_begin<kBc>(s, qt.rank, qhi);
-  if (cur.v < cur.nv) {
+  int64_t left;  // key tiles of this split still to visit
+  TileCursor cur = split_cursor<kBc>(s, qt.rank, qhi, wi.split, p.n_splits, &left);
+  if (left > 0) {
     load_tile(cur);
     store_tile(0);
   }
   int buf = 0;
-  while (cur.v < cur.nv) {
+  for (; left > 0; --left) {
     TileCursor nxt = cur;
     cursor_next<kBc>(nxt, s, qt.rank, qhi);
-    const bool has_next = nxt.v < nxt.nv;
+    const bool has_next = left > 1;
     if (has_next) load_tile(nxt);
     __syncthreads();
 
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
         f32x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * inv;
-        *(f32x4*)((float*)out + orow * D + d0) = o4;
+        *(f32x4*)((float*)out + wi.split * p.split_out_stride + orow * D + d0) = o4;
       } else {
         v4 o4;
 #pragma unroll
@@ -292,14 +294,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
         *(v4*)((E*)out + orow * D + d0) = o4;
       }
     }
-  if (hl == 0) lse[orow] = seen ? m_run * kLn2 + logf(l_tot) : kNegInf;
+  if (hl == 0)
+    lse[wi.split * p.split_lse_stride + orow] = seen ? m_run * kLn2 + logf(l_tot) : kNegInf;
 }
 
 template <typename TT, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse,
                     bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
   using E = typename TT::elem;
-  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq;
+  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq * p.n_splits;
   if (blocks <= 0) return hipSuccess;
   if (out_f32)
     hipLaunchKernelGGL((fwd_mfma_kernel<TT, D, true>), dim3((unsigned)blocks), dim3(kThreads),

@@ -110,8 +110,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
 
   // ---- work item -------------------------------------------------------
   const int32_t BH = p.B * p.Hq;
-  const int32_t bh = xcd_head_swizzle((int32_t)(blockIdx.x % BH), BH);
-  const int32_t t_lin = blockIdx.x / BH;
+  const WorkItem wi = work_item(BH, p.n_splits);
+  const int32_t bh = xcd_head_swizzle(wi.bh, BH);
+  const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
   const QTile qt = query_tile(s, t_lin);
   const int64_t qhi = qt.pos0 + qt.rows - 1;
@@ -203,9 +204,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   }
 
   // ---- tile bookkeeping ----------------------------------------------------
-  const int T = (int)count_live_tiles<BC>(s, qt.rank, qhi);  // tiles of this work item
-  TileCursor cdma = cursor_begin<BC>(s, qt.rank, qhi);        // next tile to request
-  TileCursor cqk = cdma;                                      // next tile this group scores
+  int64_t n_tiles;  // key tiles of this work item (of its split)
+  TileCursor cdma = split_cursor<BC>(s, qt.rank, qhi, wi.split, p.n_splits, &n_tiles);
+  const int T = (int)n_tiles;
+  TileCursor cqk = cdma;  // next tile this group scores; cdma: next tile to request
   int n_req = 0;
   // plan the next tile's DMA (none once all T tiles are requested)
   auto plan_next = [&]() {
@@ -417,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
         f32x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * inv;
-        *(f32x4*)((float*)out + orow * D + d0) = o4;
+        *(f32x4*)((float*)out + wi.split * p.split_out_stride + orow * D + d0) = o4;
       } else {
         v4 o4;
 #pragma unroll
@@ -425,14 +427,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
         *(v4*)((E*)out + orow * D + d0) = o4;
       }
     }
-  if (hl == 0) lse[orow] = seen ? m_run * kLn2 + logf(l_tot) : kNegInf;
+  if (hl == 0)
+    lse[wi.split * p.split_lse_stride + orow] = seen ? m_run * kLn2 + logf(l_tot) : kNegInf;
 }
 
 template <typename TT>
 hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse,
                     bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
   using E = typename TT::elem;
-  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq;
+  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq * p.n_splits;
   if (blocks <= 0) return hipSuccess;
   if (out_f32)
     hipLaunchKernelGGL((fwd_mfma128_kernel<TT, true>), dim3((unsigned)blocks), dim3(kThreads),

@@ -14,6 +14,13 @@ struct FwdParams {
   int64_t Nq;        // query rows in q (per batch)
   int64_t Nk;        // key/value rows in k, v (per batch)
   float c;           // scale * log2(e): scores are exponentiated with exp2
+  // Split-KV: the live key tiles of every query tile are divided into
+  // n_splits contiguous ranges, one workgroup each; split s writes its
+  // normalised partial (fp32) at out + s * split_out_stride and its lse at
+  // lse + s * split_lse_stride.  n_splits = 1: no split, strides unused.
+  int32_t n_splits;
+  int64_t split_out_stride;
+  int64_t split_lse_stride;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -130,6 +137,47 @@ __device__ __forceinline__ int64_t count_live_tiles(const Sched& s, int32_t rank
   const int32_t nv = num_visits(s);
   for (int32_t v = 0; v < nv; ++v) n += live_tiles(visit(s, rank, v), qhi, s.causal, BC);
   return n;
+}
+
+// Cursor on live tile number t (0-based) of a query tile, or past the end.
+template <int BC>
+__device__ __forceinline__ TileCursor cursor_at(const Sched& s, int32_t rank, int64_t qhi,
+                                                int64_t t) {
+  TileCursor c = cursor_begin<BC>(s, rank, qhi);
+  while (c.v < c.nv && t >= c.nt - c.t) {
+    t -= c.nt - c.t;
+    c.t = c.nt;
+    cursor_settle<BC>(c, s, rank, qhi);
+  }
+  if (c.v < c.nv) c.t += t;
+  return c;
+}
+
+// Work item of this workgroup: (batch * head, query tile, key split); the
+// (batch, head) index runs fastest, then the split, then the query tile.
+struct WorkItem {
+  int32_t bh, t_lin, split;
+};
+__device__ __forceinline__ WorkItem work_item(int32_t BH, int32_t n_splits) {
+  const uint32_t id = blockIdx.x;
+  const uint32_t r = id / (uint32_t)BH;
+  WorkItem w;
+  w.bh = (int32_t)(id % (uint32_t)BH);
+  w.t_lin = (int32_t)(r / (uint32_t)n_splits);
+  w.split = (int32_t)(r % (uint32_t)n_splits);
+  return w;
+}
+
+// First live tile of this split and the number of tiles it takes: split s of
+// n covers tiles [T s / n, T (s+1) / n) of the T live tiles.
+template <int BC>
+__device__ __forceinline__ TileCursor split_cursor(const Sched& s, int32_t rank, int64_t qhi,
+                                                   int32_t split, int32_t n_splits,
+                                                   int64_t* count) {
+  const int64_t T = count_live_tiles<BC>(s, rank, qhi);
+  const int64_t b0 = T * split / n_splits, b1 = T * (split + 1) / n_splits;
+  *count = b1 - b0;
+  return cursor_at<BC>(s, rank, qhi, b0);
 }
 
 template <int BC>

@@ -29,4 +29,10 @@ hipError_t launch_merge(float* out, float* lse, const float* blk_out, const floa
                         int B, int H, int64_t Nq, int64_t Nb, int64_t row_off, int d,
                         hipStream_t stream);
 
+// n-way log-sum-exp merge of split-KV partials (rows = B*Nq*H; split s at
+// ws_out + s*rows*d, ws_lse + s*rows) into out (input type) and lse.
+hipError_t launch_split_reduce(int dtype, int d, void* out, float* lse, const float* ws_out,
+                               const float* ws_lse, int n_splits, int64_t rows,
+                               hipStream_t stream);
+
 }  // namespace rattn

@@ -58,6 +58,70 @@ __global__ __launch_bounds__(256) void merge_kernel(float* __restrict__ out,
   if (c4 == 0) lse[orow] = l_new;
 }
 
+// n-way form for split-KV: rows = B*Nq*H; split s holds its normalised
+// partial at ws_out + s*rows*D and its lse at ws_lse + s*rows.  out gets the
+// merged result in the input type, lse the merged lse.
+template <typename TT, int D>
+__global__ __launch_bounds__(256) void split_reduce_kernel(void* __restrict__ out,
+                                                           float* __restrict__ lse,
+                                                           const float* __restrict__ ws_out,
+                                                           const float* __restrict__ ws_lse,
+                                                           int32_t n_splits, int64_t rows) {
+  constexpr int LPR = D / 4;
+  static_assert(64 % LPR == 0, "a row must not straddle wavefronts");
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = g / LPR;
+  const int c4 = (int)(g % LPR);
+  if (row >= rows) return;
+  float m = kNegInf;
+  for (int32_t s = 0; s < n_splits; ++s) m = fmaxf(m, ws_lse[s * rows + row]);
+  f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+  float l_new = kNegInf;
+  if (m != kNegInf) {
+    float z = 0.f;
+    for (int32_t s = 0; s < n_splits; ++s) {
+      const float w = expf(ws_lse[s * rows + row] - m);
+      z += w;
+      o += *(const f32x4*)(ws_out + (s * rows + row) * D + 4 * c4) * w;
+    }
+    o *= 1.f / z;
+    l_new = m + logf(z);
+  }
+  if constexpr (sizeof(typename TT::elem) == 4) {
+    *(f32x4*)((float*)out + row * D + 4 * c4) = o;
+  } else {
+    typedef typename TT::elem E;
+    typedef E e4 __attribute__((ext_vector_type(4)));
+    e4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = to_elem<TT>(o[e]);
+    *(e4*)((E*)out + row * D + 4 * c4) = v;
+  }
+  if (c4 == 0) lse[row] = l_new;
+}
+
+template <typename TT, int D>
+hipError_t launch_reduce(void* out, float* lse, const float* ws_out, const float* ws_lse,
+                         int n_splits, int64_t rows, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows * (D / 4) + 255) / 256;
+  hipLaunchKernelGGL((split_reduce_kernel<TT, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     out, lse, ws_out, ws_lse, (int32_t)n_splits, rows);
+  return hipGetLastError();
+}
+
+template <typename TT>
+hipError_t launch_reduce_t(int d, void* out, float* lse, const float* ws_out,
+                           const float* ws_lse, int n_splits, int64_t rows, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_reduce<TT, 16>(out, lse, ws_out, ws_lse, n_splits, rows, stream);
+    case 32: return launch_reduce<TT, 32>(out, lse, ws_out, ws_lse, n_splits, rows, stream);
+    case 64: return launch_reduce<TT, 64>(out, lse, ws_out, ws_lse, n_splits, rows, stream);
+    case 128: return launch_reduce<TT, 128>(out, lse, ws_out, ws_lse, n_splits, rows, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int D>
 hipError_t launch_d(float* out, float* lse, const float* blk_out, const float* blk_lse, int B,
                     int H, int64_t Nq, int64_t Nb, int64_t row_off, hipStream_t stream) {
@@ -80,6 +144,17 @@ hipError_t launch_merge(float* out, float* lse, const float* blk_out, const floa
     case 32: return launch_d<32>(out, lse, blk_out, blk_lse, B, H, Nq, Nb, row_off, stream);
     case 64: return launch_d<64>(out, lse, blk_out, blk_lse, B, H, Nq, Nb, row_off, stream);
     case 128: return launch_d<128>(out, lse, blk_out, blk_lse, B, H, Nq, Nb, row_off, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_split_reduce(int dtype, int d, void* out, float* lse, const float* ws_out,
+                               const float* ws_lse, int n_splits, int64_t rows,
+                               hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_reduce_t<F32>(d, out, lse, ws_out, ws_lse, n_splits, rows, stream);
+    case 1: return launch_reduce_t<F16>(d, out, lse, ws_out, ws_lse, n_splits, rows, stream);
+    case 2: return launch_reduce_t<Bf16>(d, out, lse, ws_out, ws_lse, n_splits, rows, stream);
     default: return hipErrorInvalidValue;
   }
 }

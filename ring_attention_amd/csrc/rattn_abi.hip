@@ -15,6 +15,8 @@ namespace {
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+constexpr int kMaxSplits = 64;  // split-KV: most key splits per query tile
+
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
 // a*b without signed overflow, for sizes that are all >= 0.
@@ -81,6 +83,9 @@ FwdParams make_params(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, float scal
   p.Nq = Nq;
   p.Nk = Nk;
   p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  p.n_splits = 1;
+  p.split_out_stride = 0;
+  p.split_lse_stride = 0;
   return p;
 }
 
@@ -101,10 +106,13 @@ int dispatch(int dtype, int d, const void* q, const void* k, const void* v, void
 
 using namespace rattn;
 
-extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                         int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d, int dtype,
-                         float scale, int causal, int n_ring_steps, int zigzag, int rank,
-                         void* stream) {
+namespace rattn {
+namespace {
+
+// Checks of rattn_fwd's arguments and its schedule (shared with rattn_fwd_split).
+int prepare_ring(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d, int dtype, int causal,
+                 int n_ring_steps, int zigzag, int rank, Sched* sched) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
   if (N < 0 || Nq < 0) return RATTN_EINVAL;
   // a pointer may be null only when its tensor is empty
@@ -123,10 +131,9 @@ extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out,
       !aligned(lse, 4))
     return RATTN_EINVAL;
   if (!tensor_ok(B, N, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
-  if (Nq == 0) return RATTN_OK;
 
   const int br = tile_rows(dtype, d);
-  Sched s;
+  Sched& s = *sched;
   memset(&s, 0, sizeof s);
   s.W = W;
   s.causal = causal;
@@ -153,10 +160,76 @@ extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out,
         segs[n++] = QSeg{g * c, c, g * c, g < W ? g : 2 * W - 1 - g, 0};
     }
   }
-  rc = finalize(s, segs, n, br);
-  if (rc != RATTN_OK) return rc;
+  return finalize(s, segs, n, br);
+}
+
+}  // namespace
+}  // namespace rattn
+
+extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d, int dtype,
+                         float scale, int causal, int n_ring_steps, int zigzag, int rank,
+                         void* stream) {
+  Sched s;
+  const int rc = prepare_ring(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, causal,
+                              n_ring_steps, zigzag, rank, &s);
+  if (rc != RATTN_OK || Nq == 0) return rc;
   const FwdParams p = make_params(B, Hq, Hkv, Nq, N, resolve_scale(scale, d));
   return dispatch(dtype, d, q, k, v, out, lse, false, p, s, (int64_t)s.n_tiles * B * Hq, stream);
+}
+
+extern "C" int rattn_fwd_split(const void* q, const void* k, const void* v, void* out,
+                               float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d,
+                               int dtype, float scale, int causal, int n_ring_steps, int zigzag,
+                               int rank, int n_splits, float* ws, int64_t ws_floats,
+                               void* stream) {
+  if (n_splits < 1) return RATTN_EINVAL;
+  if (n_splits > kMaxSplits) return RATTN_EUNSUPPORTED;
+  Sched s;
+  int rc = prepare_ring(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, causal, n_ring_steps,
+                        zigzag, rank, &s);
+  if (rc != RATTN_OK || Nq == 0) return rc;
+  if (n_splits == 1)
+    return rattn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, scale, causal,
+                     n_ring_steps, zigzag, rank, stream);
+  const int64_t rows = (int64_t)B * Nq * Hq;
+  int64_t need;
+  if (!mul_ok(rows, (int64_t)d + 1, &need) || !mul_ok(need, n_splits, &need))
+    return RATTN_EUNSUPPORTED;
+  if (!ws || ws_floats < need || !aligned(ws, 16)) return RATTN_EINVAL;
+  FwdParams p = make_params(B, Hq, Hkv, Nq, N, resolve_scale(scale, d));
+  p.n_splits = n_splits;
+  p.split_out_stride = rows * d;
+  p.split_lse_stride = rows;
+  float* ws_out = ws;
+  float* ws_lse = ws + (int64_t)n_splits * rows * d;
+  rc = dispatch(dtype, d, q, k, v, ws_out, ws_lse, true, p, s,
+                (int64_t)s.n_tiles * B * Hq * n_splits, stream);
+  if (rc != RATTN_OK) return rc;
+  if ((rows * (d / 4) + 255) / 256 > INT32_MAX) return RATTN_EUNSUPPORTED;
+  const hipError_t e = launch_split_reduce(dtype, d, out, lse, ws_out, ws_lse, n_splits, rows,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+}
+
+extern "C" int rattn_split_hint(int B, int Hq, int64_t Nq, int64_t N, int d, int dtype,
+                                int n_ring_steps, int zigzag, int rank, int n_cu) {
+  (void)zigzag;
+  (void)rank;
+  if (B < 1 || Hq < 1 || Nq < 1 || N < 1 || n_cu < 1 || n_ring_steps < 1) return 1;
+  if (check_dtype_d(dtype, d) != RATTN_OK) return 1;
+  const int64_t br = tile_rows(dtype, d);
+  const int64_t items = (Nq + br - 1) / br * B * Hq;
+  // Half as many workgroups as compute units already hides most of the
+  // split's cost (partials written and merged); measured on 4096 x 4096,
+  // one head: 8 splits (128 workgroups) beat 4, 16 and 32.
+  const int64_t want = ((int64_t)n_cu + 1) / 2;
+  if (items >= want) return 1;
+  int64_t n = (want + items - 1) / items;
+  const int64_t key_tiles = (N + 63) / 64;  // keep at least 8 key tiles per split
+  if (n > key_tiles / 8) n = key_tiles / 8;
+  if (n > kMaxSplits) n = kMaxSplits;
+  return n < 1 ? 1 : (int)n;
 }
 
 extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk,

@@ -75,6 +75,43 @@ def test_fwd_empty_is_ok_without_launch(rattn_lib):
     assert fwd(rattn_lib, k=0, N=64, Nq=64) == EINVAL
 
 
+def fwd_split(lib, n_splits=4, ws=P[5], ws_floats=None, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4], B=1, Hq=2, Hkv=2, Nq=64, N=64, d=64,
+             dtype=2, scale=0.0, causal=1, W=1, zigzag=0, rank=-1)
+    a.update(kw)
+    need = n_splits * a["B"] * a["Nq"] * a["Hq"] * (a["d"] + 1)
+    return lib.rattn_fwd_split(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                               a["Hkv"], a["Nq"], a["N"], a["d"], a["dtype"], a["scale"],
+                               a["causal"], a["W"], a["zigzag"], a["rank"], n_splits, ws,
+                               need if ws_floats is None else ws_floats, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_splits=0), EINVAL), (dict(n_splits=65), EUNSUP), (dict(ws=0), EINVAL),
+    (dict(ws_floats=100), EINVAL), (dict(ws=P[5] + 4), EINVAL), (dict(q=0), EINVAL),
+    (dict(d=48), EUNSUP), (dict(W=3), EINVAL),
+])
+def test_fwd_split_rejects(rattn_lib, kw, status):
+    assert fwd_split(rattn_lib, **kw) == status
+
+
+def test_fwd_split_empty_is_ok_without_launch(rattn_lib):
+    assert fwd_split(rattn_lib, N=0, Nq=0) == OK
+    assert fwd_split(rattn_lib, N=0, Nq=0, ws=0) == OK
+
+
+def test_split_hint(rattn_lib):
+    h = rattn_lib.rattn_split_hint
+    # (B, Hq, Nq, N, d, dtype, W, zigzag, rank, n_cu)
+    assert h(1, 1, 4096, 4096, 128, 2, 1, 0, -1, 256) == 8   # 16 tiles of 256 rows -> 128 items
+    assert h(1, 8, 16384, 131072, 128, 2, 8, 1, 2, 256) == 1   # 512 query tiles already
+    assert h(1, 1, 256, 256, 128, 2, 1, 0, -1, 256) == 1       # 4 key tiles: no split
+    assert h(1, 1, 1024, 1024, 128, 2, 1, 0, -1, 256) == 2     # 16 key tiles: at most 2
+    assert h(1, 1, 64, 1 << 20, 64, 1, 1, 0, -1, 256) == 64    # capped at 64
+    assert h(1, 1, 4096, 4096, 48, 2, 1, 0, -1, 256) == 1      # unsupported d
+    assert h(0, 1, 4096, 4096, 128, 2, 1, 0, -1, 256) == 1
+
+
 def seg(a, b):
     return (ctypes.c_int64 * 2)(a, b)
 

@@ -349,6 +349,60 @@ def test_d128_step_query_tiles_without_keys(gpu):
     assert np.isneginf(host(lse)[0, :300]).all() and (host(out)[0, :300] == 0).all()
 
 
+# --------------------------------------------------------------------------
+# split-KV: the key tiles of every query tile over n_splits workgroups, then
+# the n-way log-sum-exp merge
+
+
+def run_split_check(q, k, v, causal, W, zigzag, rank, n_splits, what, tol_o=None):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out, lse = binding.fwd_split(qd, kd, vd, causal=causal, n_ring_steps=W, zigzag=zigzag,
+                                 rank=rank, n_splits=n_splits)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(q, k, v, causal=causal,
+                                    q_pos=q_positions(k.shape[1], W, zigzag, rank))
+    return compare(host(out), host(lse), ref_o, ref_l, q.dtype, tol_o, what)
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 16), (torch.float16, 32),
+                                     (torch.bfloat16, 64), (torch.bfloat16, 128),
+                                     (torch.float16, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_splits", [2, 5, 64])
+def test_split_kv(gpu, dtype, d, causal, n_splits):
+    # 600 rows: ragged in every tile size; 64 splits leave some splits empty
+    q, k, v = workloads.make_qkv(1, 600, 600, 2, 1, d, dtype, seed=50 + d + n_splits)
+    run_split_check(q, k, v, causal, 1, False, -1, n_splits,
+                    f"split-KV {dtype} d={d} causal={causal} splits={n_splits}")
+
+
+@pytest.mark.parametrize("W,zigzag,rank", [(4, True, 1), (4, True, -1), (3, False, 2)])
+def test_split_kv_ring_layouts(gpu, W, zigzag, rank):
+    N = 2 * W * 96 if zigzag else W * 128
+    q, k, v = workloads.make_qkv(1, N, N, 2, 2, 128, torch.bfloat16, seed=60 + W)
+    if rank >= 0:
+        q = ring.shard(q, W, zigzag, rank)
+    run_split_check(q, k, v, True, W, zigzag, rank, 3, f"split-KV W={W} zz={zigzag} r={rank}")
+
+
+def test_split_kv_workload2_with_hint(gpu):
+    w = workloads.workload(2)
+    q, k, v = workloads.make_inputs(w)
+    qd = q.to("cuda:0")
+    n = binding.split_hint(qd, k.to("cuda:0"))
+    note(f"case {w.name}, {n} splits")
+    assert n > 1
+    run_split_check(q, k, v, w.causal, w.W, w.zigzag, w.rank, n, f"{w.name} split {n}")
+
+
+def test_split_kv_one_split_is_fwd(gpu):
+    q, k, v = workloads.make_qkv(1, 300, 300, 2, 2, 128, torch.bfloat16, seed=70, device=gpu)
+    a, la = binding.fwd(q, k, v, causal=True)
+    b, lb = binding.fwd_split(q, k, v, causal=True, n_splits=1)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 def test_merge_kernel(gpu, d):
     dev = torch.device("cuda:0")
