@@ -6,8 +6,10 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 one simulated device's share of an 8-way ZigZag causal ring at its real shape
 (total sequence 131072 in 16 chunks of 8192, the device's query shard =
 chunks {2, 13}, 8 heads, d = 128, bf16, N(0,1)), run as the ring runs it:
-8 step-kernel launches over the 8 key/value shards in ring order, each
-followed (after the first) by a log-sum-exp merge into the running output.
+8 step-kernel launches over the 8 key/value shards in ring order; after the
+first, each merges its result into the running output with the log-sum-exp
+correction in its epilogue (steps_separate_merge times the same ring with the
+merges as launches of their own).
 
 `value` is causal-adjusted TFLOP/s: 4*d FLOP per visible (query, key) pair
 per query head (2d for QK^T, 2d for PV; exponentials and masked work are not
@@ -319,9 +321,10 @@ def main():
     pairs = sum(step_pairs)
     flop_per_step = 4 * d * Hq * w.B * pairs
 
-    def one_step(hook=None):
+    def one_step(hook=None, fused_merge=True):
         kw = {} if hook is None else {"hook": hook}
-        return ring.ring_forward_steps(q, ks, vs, W, True, rank, causal=True, **kw)
+        return ring.ring_forward_steps(q, ks, vs, W, True, rank, causal=True,
+                                       fused_merge=fused_merge, **kw)
 
     for _ in range(args.warmup):
         one_step()
@@ -357,9 +360,20 @@ def main():
         one_step(hook)
     n_launch = len(kern.pairs)
     kern_ms = kern.total_ms() / n_launch
-    merge_ms = merge_t.total_ms() / max(1, len(merge_t.pairs))
     flop_per_launch = 4 * d * Hq * w.B * pairs / len(plan)
     achieved = flop_per_launch / (kern_ms * 1e-3) / 1e12
+
+    # the same ring with each merge as its own launch (step kernels write
+    # float32 partials, rattn_merge folds them in)
+    for _ in range(args.warmup):
+        one_step(fused_merge=False)
+    sep = Timer(torch)
+    for _ in range(args.steps):
+        sep(lambda: one_step(fused_merge=False))
+    sep_ms = sep.total_ms() / args.steps
+    for _ in range(args.steps):
+        one_step(hook, fused_merge=False)
+    merge_ms = merge_t.total_ms() / max(1, len(merge_t.pairs))
 
     # fused single launch of the same share
     fo = fl = None
@@ -388,7 +402,8 @@ def main():
         "data": "synthetic: N(0,1) bf16 q/k/v from a seeded torch generator, resident in HBM",
         "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "N": N, "Hq": Hq, "Hkv": w.Hkv,
                    "d": d, "causal": True, "ring": W, "zigzag": True, "rank": rank,
-                   "mode": "8 ring-step launches + 7 LSE merges",
+                   "mode": "8 ring-step launches; steps 2-8 merge into the running "
+                           "(out, lse) in the kernel epilogue (LSE merge fused)",
                    "visible_pairs_per_head": pairs,
                    "flop_per_step": flop_per_step,
                    # the usual causal estimate, half of all (query, key) pairs
@@ -398,7 +413,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": stored_traffic(), "kernel": STEP_KERNEL,
                      "avg_launch_ms": round(kern_ms, 4), "launches": n_launch},
-        "merge_avg_ms": round(merge_ms, 4),
+        "steps_separate_merge": {"value": round(flop_per_step / (sep_ms * 1e-3) / 1e12, 2),
+                                 "ms": round(sep_ms, 4), "merge_avg_ms": round(merge_ms, 4)},
         "fused": {"value": round(fused_value, 2), "ms": round(fused_ms, 4),
                   "pct_of_peak": round(100 * fused_value / PEAK_BF16_TFLOPS, 2)},
     }

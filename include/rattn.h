@@ -97,6 +97,24 @@ RATTN_API int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk
                    const int64_t* k_seg_start, const int64_t* k_seg_len, void* stream);
 
 /*
+ * One ring step merged into the running result: rattn_fwd_step's partial for
+ * query rows i in [0, Nq) of q, merged by the log-sum-exp correction (Twinkle
+ * page, update_out_and_lse; same function as rattn_merge) into
+ *   (out, lse)[b, row_off + i, h],  out [B, Nq_out, Hq, d] float32,
+ *   lse [B, Nq_out, Hq] float32,
+ * in the kernel's epilogue (one launch instead of a step and a merge).
+ * Requires row_off + Nq <= Nq_out; out/lse must not overlap q, k, v.  A row
+ * that sees no key leaves (out, lse) unchanged.  Other arguments and errors
+ * as rattn_fwd_step.
+ */
+RATTN_API int rattn_fwd_step_merge(const void* q, const void* k_blk, const void* v_blk,
+                                   float* out, float* lse, int B, int Hq, int Hkv, int64_t Nq,
+                                   int64_t Nk, int d, int dtype, float scale, int causal,
+                                   const int64_t* q_seg_start, const int64_t* q_seg_len,
+                                   const int64_t* k_seg_start, const int64_t* k_seg_len,
+                                   int64_t Nq_out, int64_t row_off, void* stream);
+
+/*
  * In-place log-sum-exp merge (Twinkle page, update_out_and_lse; computed as
  * lse' = logaddexp(lse, blk_lse), out' = e^(lse-lse') out + e^(blk_lse-lse') blk_out):
  *   (out, lse)[b, row_off + i, h] <- (out, lse)[b, row_off + i, h]

@@ -20,8 +20,8 @@ RATTN_OK, RATTN_EINVAL, RATTN_EUNSUPPORTED, RATTN_EHIP = 0, -1, -2, -3
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # Exported symbols, in the order include/rattn.h declares them.
-EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_merge", "rattn_fwd_split", "rattn_split_hint",
-           "rattn_status_string")
+EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_fwd_step_merge", "rattn_merge",
+           "rattn_fwd_split", "rattn_split_hint", "rattn_status_string")
 
 
 class RattnError(RuntimeError):
@@ -52,6 +52,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rattn_fwd_step.restype = i32
     lib.rattn_fwd_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
                                    i32, i64p, i64p, i64p, i64p, vp]
+    lib.rattn_fwd_step_merge.restype = i32
+    lib.rattn_fwd_step_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32,
+                                         f32, i32, i64p, i64p, i64p, i64p, i64, i64, vp]
     lib.rattn_merge.restype = i32
     lib.rattn_merge.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp]
     lib.rattn_fwd_split.restype = i32
@@ -165,6 +168,40 @@ def fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
     return out, lse
 
 
+def _segs(pairs):
+    """Up to two (start_position, length) pairs as two host int64[2] arrays."""
+    pairs = list(pairs) + [(0, 0)] * (2 - len(pairs))
+    if len(pairs) != 2:
+        raise ValueError("at most two segments")
+    starts = (ctypes.c_int64 * 2)(*[int(p[0]) for p in pairs])
+    lens = (ctypes.c_int64 * 2)(*[int(p[1]) for p in pairs])
+    return starts, lens
+
+
+def fwd_step_merge(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, causal: bool,
+                   q_segs, k_segs, out: torch.Tensor, lse: torch.Tensor, row_off: int = 0,
+                   scale: float | None = None):
+    """One ring step merged into the running float32 (out, lse) at rows
+    [row_off, row_off + Nq) (rattn_fwd_step_merge); returns (out, lse)."""
+    _qkv(q, k_blk, v_blk)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k_blk.shape[1], k_blk.shape[2]
+    for name, t in (("out", out), ("lse", lse)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous float32 tensor on q's device")
+    if out.dim() != 4 or out.shape[0] != B or out.shape[2:] != (Hq, d) or \
+            lse.shape != out.shape[:3]:
+        raise ValueError("out must be [B, Nq_out, Hq, d] and lse [B, Nq_out, Hq]")
+    qs, ql = _segs(q_segs)
+    kst, kl = _segs(k_segs)
+    rc = load_library().rattn_fwd_step_merge(
+        q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+        Hkv, Nq, Nk, d, DTYPE_CODES[q.dtype], _scale(scale), int(bool(causal)), qs, ql, kst, kl,
+        out.shape[1], int(row_off), _stream(q))
+    _check("rattn_fwd_step_merge", rc)
+    return out, lse
+
+
 def fwd_step(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, causal: bool,
              q_segs, k_segs, scale: float | None = None,
              out_part: torch.Tensor | None = None, lse_part: torch.Tensor | None = None):
@@ -176,17 +213,8 @@ def fwd_step(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, causal: 
     _qkv(q, k_blk, v_blk)
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k_blk.shape[1], k_blk.shape[2]
-
-    def segs(pairs):
-        pairs = list(pairs) + [(0, 0)] * (2 - len(pairs))
-        if len(pairs) != 2:
-            raise ValueError("at most two segments")
-        starts = (ctypes.c_int64 * 2)(*[int(p[0]) for p in pairs])
-        lens = (ctypes.c_int64 * 2)(*[int(p[1]) for p in pairs])
-        return starts, lens
-
-    qs, ql = segs(q_segs)
-    kst, kl = segs(k_segs)
+    qs, ql = _segs(q_segs)
+    kst, kl = _segs(k_segs)
     if out_part is None:
         out_part = torch.empty((B, Nq, Hq, d), dtype=torch.float32, device=q.device)
     if lse_part is None:

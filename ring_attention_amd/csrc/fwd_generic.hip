@@ -106,18 +106,28 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(
   if (!q_valid) return;
   const bool seen = l > 0.f;
   const float inv = seen ? 1.f / l : 0.f;
-  const int64_t o_off = (((int64_t)b * p.Nq + qt.row0 + lane) * p.Hq + hq) * D;
+  const float lse_n = seen ? m * kLn2 + logf(l) : kNegInf;
+  const int64_t orow = ((int64_t)b * p.out_rows + p.out_row_off + qt.row0 + lane) * p.Hq + hq;
+  const int64_t o_off = orow * D;
+  float* lse_w = lse + wi.split * p.split_lse_stride;
+  const bool merging = OUT_F32 && p.merge_out;
+  const MergeW mw = merging ? merge_weights(lse_w[orow], lse_n) : MergeW{0.f, 1.f, lse_n};
   if (OUT_F32) {
     float* o = (float*)out + wi.split * p.split_out_stride + o_off;
+    const float f_n = mw.f_n * inv;
+    if (merging) {
 #pragma unroll
-    for (int t = 0; t < D; ++t) o[t] = acc[t] * inv;
+      for (int t = 0; t < D; ++t) o[t] = acc[t] * f_n + o[t] * mw.f_r;
+    } else {
+#pragma unroll
+      for (int t = 0; t < D; ++t) o[t] = acc[t] * f_n;
+    }
   } else {
     E* o = (E*)out + o_off;
 #pragma unroll
     for (int t = 0; t < D; ++t) o[t] = to_elem<TT>(acc[t] * inv);
   }
-  lse[wi.split * p.split_lse_stride + ((int64_t)b * p.Nq + qt.row0 + lane) * p.Hq + hq] =
-      seen ? m * kLn2 + logf(l) : kNegInf;
+  lse_w[orow] = mw.lse;
 }
 
 // Host-side launchers (declared in launch.h).

@@ -276,7 +276,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   if (!q_valid) return;
   const bool seen = l_tot > 0.f;
   const float inv = seen ? 1.f / l_tot : 0.f;
-  const int64_t orow = ((int64_t)b * p.Nq + qt.row0 + my_q) * p.Hq + hq;
+  const float lse_n = seen ? m_run * kLn2 + logf(l_tot) : kNegInf;
+  const int64_t orow = ((int64_t)b * p.out_rows + p.out_row_off + qt.row0 + my_q) * p.Hq + hq;
+  float* out_f = (float*)out + wi.split * p.split_out_stride;
+  float* lse_w = lse + wi.split * p.split_lse_stride;
+  const bool merging = OUT_F32 && p.merge_out;
+  const MergeW mw = merging ? merge_weights(lse_w[orow], lse_n) : MergeW{0.f, 1.f, lse_n};
+  const float f_n = mw.f_n * inv;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -285,8 +291,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
       if (OUT_F32) {
         f32x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * inv;
-        *(f32x4*)((float*)out + wi.split * p.split_out_stride + orow * D + d0) = o4;
+        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * f_n;
+        f32x4* dst = (f32x4*)(out_f + orow * D + d0);
+        if (merging) o4 += *dst * mw.f_r;
+        *dst = o4;
       } else {
         v4 o4;
 #pragma unroll
@@ -294,8 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
         *(v4*)((E*)out + orow * D + d0) = o4;
       }
     }
-  if (hl == 0)
-    lse[wi.split * p.split_lse_stride + orow] = seen ? m_run * kLn2 + logf(l_tot) : kNegInf;
+  if (hl == 0) lse_w[orow] = mw.lse;
 }
 
 template <typename TT, int D>

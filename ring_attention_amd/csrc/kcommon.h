@@ -21,7 +21,28 @@ struct FwdParams {
   int32_t n_splits;
   int64_t split_out_stride;
   int64_t split_lse_stride;
+  // Output rows: query row i of this call is row out_row_off + i of the
+  // [B, out_rows, Hq] output.  merge_out = 1 (fp32 output only): log-sum-exp
+  // merge this call's normalised result into the (out, lse) already there
+  // instead of overwriting it.
+  int64_t out_rows;
+  int64_t out_row_off;
+  int32_t merge_out;
 };
+
+// Merge of a normalised partial (lse_n) into a running normalised result
+// (lse_r): out = f_r * out_r + f_n * out_n, lse = lse_out.  An empty side
+// (lse = -inf) weighs 0; two empty sides give out 0, lse -inf.  This is the
+// log-sum-exp correction applied after every ring step, in max-shifted form.
+struct MergeW {
+  float f_r, f_n, lse;
+};
+__device__ __forceinline__ MergeW merge_weights(float lse_r, float lse_n) {
+  const float m = fmaxf(lse_r, lse_n);
+  if (m == -__builtin_inff()) return MergeW{0.f, 0.f, m};
+  const float wr = expf(lse_r - m), wn = expf(lse_n - m), z = wr + wn;
+  return MergeW{wr / z, wn / z, m + logf(z)};
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

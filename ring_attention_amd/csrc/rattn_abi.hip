@@ -86,6 +86,9 @@ FwdParams make_params(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, float scal
   p.n_splits = 1;
   p.split_out_stride = 0;
   p.split_lse_stride = 0;
+  p.out_rows = Nq;
+  p.out_row_off = 0;
+  p.merge_out = 0;
   return p;
 }
 
@@ -232,18 +235,22 @@ extern "C" int rattn_split_hint(int B, int Hq, int64_t Nq, int64_t N, int d, int
   return n < 1 ? 1 : (int)n;
 }
 
-extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk,
-                              float* out_part, float* lse_part, int B, int Hq, int Hkv,
-                              int64_t Nq, int64_t Nk, int d, int dtype, float scale, int causal,
-                              const int64_t* q_seg_start, const int64_t* q_seg_len,
-                              const int64_t* k_seg_start, const int64_t* k_seg_len,
-                              void* stream) {
+namespace rattn {
+namespace {
+
+// rattn_fwd_step / rattn_fwd_step_merge: output rows [row_off, row_off + Nq)
+// of a [B, Nq_out, Hq, d] fp32 output; merge = 1 merges into it.
+int fwd_step_impl(const void* q, const void* k_blk, const void* v_blk, float* out,
+                  float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int d, int dtype,
+                  float scale, int causal, const int64_t* q_seg_start, const int64_t* q_seg_len,
+                  const int64_t* k_seg_start, const int64_t* k_seg_len, int64_t Nq_out,
+                  int64_t row_off, int merge, void* stream) {
   if (!q_seg_start || !q_seg_len || !k_seg_start || !k_seg_len) return RATTN_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
-  if (Nq < 0 || Nk < 0) return RATTN_EINVAL;
+  if (Nq < 0 || Nk < 0 || row_off < 0 || Nq_out < 0) return RATTN_EINVAL;
+  if (row_off > Nq_out || Nq > Nq_out - row_off) return RATTN_EINVAL;
   // a pointer may be null only when its tensor is empty
-  if ((Nq > 0 && (!q || !out_part || !lse_part)) || (Nk > 0 && (!k_blk || !v_blk)))
-    return RATTN_EINVAL;
+  if ((Nq > 0 && (!q || !out || !lse)) || (Nk > 0 && (!k_blk || !v_blk))) return RATTN_EINVAL;
   int rc = check_dtype_d(dtype, d);
   if (rc != RATTN_OK) return rc;
   if (causal != 0 && causal != 1) return RATTN_EINVAL;
@@ -251,10 +258,11 @@ extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_bl
     if (q_seg_len[i] < 0 || k_seg_len[i] < 0) return RATTN_EINVAL;
   if (q_seg_len[0] + q_seg_len[1] != Nq || k_seg_len[0] + k_seg_len[1] != Nk)
     return RATTN_EINVAL;
-  if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) ||
-      !aligned(out_part, 16) || !aligned(lse_part, 4))
+  if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4))
     return RATTN_EINVAL;
-  if (!tensor_ok(B, Nq > Nk ? Nq : Nk, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
+  const int64_t rows_max = std::max(std::max(Nq, Nk), Nq_out);
+  if (!tensor_ok(B, rows_max, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
   if (Nq == 0) return RATTN_OK;
 
   const int br = tile_rows(dtype, d);
@@ -270,9 +278,37 @@ extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_bl
                   QSeg{q_seg_len[0], q_seg_len[1], q_seg_start[1], 0, 0}};
   rc = finalize(s, segs, 2, br);
   if (rc != RATTN_OK) return rc;
-  const FwdParams p = make_params(B, Hq, Hkv, Nq, Nk, resolve_scale(scale, d));
-  return dispatch(dtype, d, q, k_blk, v_blk, out_part, lse_part, true, p, s,
+  FwdParams p = make_params(B, Hq, Hkv, Nq, Nk, resolve_scale(scale, d));
+  p.out_rows = Nq_out;
+  p.out_row_off = row_off;
+  p.merge_out = merge;
+  return dispatch(dtype, d, q, k_blk, v_blk, out, lse, true, p, s,
                   (int64_t)s.n_tiles * B * Hq, stream);
+}
+
+}  // namespace
+}  // namespace rattn
+
+extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk,
+                              float* out_part, float* lse_part, int B, int Hq, int Hkv,
+                              int64_t Nq, int64_t Nk, int d, int dtype, float scale, int causal,
+                              const int64_t* q_seg_start, const int64_t* q_seg_len,
+                              const int64_t* k_seg_start, const int64_t* k_seg_len,
+                              void* stream) {
+  return fwd_step_impl(q, k_blk, v_blk, out_part, lse_part, B, Hq, Hkv, Nq, Nk, d, dtype, scale,
+                       causal, q_seg_start, q_seg_len, k_seg_start, k_seg_len, Nq, 0, 0,
+                       stream);
+}
+
+extern "C" int rattn_fwd_step_merge(const void* q, const void* k_blk, const void* v_blk,
+                                    float* out, float* lse, int B, int Hq, int Hkv, int64_t Nq,
+                                    int64_t Nk, int d, int dtype, float scale, int causal,
+                                    const int64_t* q_seg_start, const int64_t* q_seg_len,
+                                    const int64_t* k_seg_start, const int64_t* k_seg_len,
+                                    int64_t Nq_out, int64_t row_off, void* stream) {
+  return fwd_step_impl(q, k_blk, v_blk, out, lse, B, Hq, Hkv, Nq, Nk, d, dtype, scale, causal,
+                       q_seg_start, q_seg_len, k_seg_start, k_seg_len, Nq_out, row_off, 1,
+                       stream);
 }
 
 extern "C" int rattn_merge(float* out, float* lse, const float* blk_out, const float* blk_lse,

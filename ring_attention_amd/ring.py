@@ -1,9 +1,11 @@
 """One simulated device of the ring, run step by step on one GPU.
 
-Each step is one call of the step kernel (rattn_fwd_step) on the key/value
-shard the device holds at that step, followed by a log-sum-exp merge
-(rattn_merge) into the running (out, lse) -- the structure of the Twinkle
-forward pass ("Sequence parallel and Ring Attention", forward-pass section).
+Each step is one call of the step kernel on the key/value shard the device
+holds at that step, with a log-sum-exp merge into the running (out, lse) --
+the structure of the Twinkle forward pass ("Sequence parallel and Ring
+Attention", forward-pass section).  The merge runs in the step kernel's
+epilogue (rattn_fwd_step_merge) or as its own launch (rattn_fwd_step, then
+rattn_merge).
 The fused entry point (rattn_fwd) computes the same thing in one launch.
 
 Ring order: at step s device r holds the shard of device (r - s) mod W
@@ -52,13 +54,16 @@ def _direct(kind, fn):
 
 def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag: bool,
                        rank: int, causal: bool = True, scale: float | None = None,
-                       hook=_direct):
+                       hook=_direct, fused_merge: bool = True):
     """Run device ``rank``'s W ring steps; returns float32 (out, lse).
 
     q_shard [B, Nq, Hq, d] is the device's query shard; k_shards[src] and
     v_shards[src] are the shards every device would send (see ``shard``).
-    hook(kind, fn) wraps every library call ("step" or "merge") and must
-    return fn(); a benchmark uses it to time the launches.
+    fused_merge: steps after the first merge into the running result in the
+    step kernel's epilogue (rattn_fwd_step_merge); else each writes a partial
+    that rattn_merge folds in.  hook(kind, fn) wraps every library call
+    ("step" or "merge") and must return fn(); a benchmark uses it to time
+    the launches.
     """
     N = sum(k.shape[1] for k in k_shards)
     B, Nq, Hq, d = q_shard.shape
@@ -91,6 +96,10 @@ def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag
             # the first step writes the running result directly
             out, lse = hook("step", lambda: binding.fwd_step(qv, kb, vb, step_causal, qr, kr,
                                                              scale))
+            continue
+        if fused_merge:
+            hook("step", lambda: binding.fwd_step_merge(qv, kb, vb, step_causal, qr, kr, out, lse,
+                                                        row_off=row_off, scale=scale))
             continue
         bo, bl = hook("step", lambda: binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale))
         hook("merge", lambda: binding.merge(out, lse, bo, bl, row_off=row_off))

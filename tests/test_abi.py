@@ -132,6 +132,20 @@ def test_fwd_step_rejects(rattn_lib, kw, status):
     assert step(rattn_lib, **kw) == status
 
 
+def step_merge(lib, Nq=32, Nq_out=64, off=0, q=P[0], out=P[3]):
+    return lib.rattn_fwd_step_merge(q, P[1], P[2], out, P[4], 1, 4, 2, Nq, 32, 128, 1, 0.0, 1,
+                                    seg(0, 0), seg(Nq, 0), seg(0, 0), seg(32, 0), Nq_out, off,
+                                    None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(off=40), EINVAL), (dict(off=-1), EINVAL), (dict(Nq_out=16), EINVAL),
+    (dict(Nq_out=-1), EINVAL), (dict(q=0), EINVAL), (dict(out=P[3] + 4), EINVAL),
+])
+def test_fwd_step_merge_rejects(rattn_lib, kw, status):
+    assert step_merge(rattn_lib, **kw) == status
+
+
 def test_fwd_step_empty_is_ok_without_launch(rattn_lib):
     assert step(rattn_lib, Nq=0, ql=(0, 0)) == OK
     assert step(rattn_lib, Nq=0, ql=(0, 0), q=0, out=0) == OK

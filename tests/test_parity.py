@@ -141,6 +141,11 @@ def test_workload4_ring_steps_and_merge(workload4_inputs):
     rows = sampled_rows(w)
     check_sampled(out.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu(), rows,
                   layouts.zigzag_shard_positions(w.N, w.W, w.rank), w, w.name + " steps")
+    # merges as their own launches: the same result up to rounding order
+    so, sl = ring.ring_forward_steps(q, ks, vs, w.W, True, w.rank, causal=True,
+                                     fused_merge=False)
+    torch.cuda.synchronize()
+    assert (so - out).abs().max().item() <= 1e-5 and (sl - lse).abs().max().item() <= 1e-5
     # fused and step-by-step agree closely on every row
     fo, fl = binding.fwd(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=w.rank)
     torch.cuda.synchronize()
@@ -205,8 +210,9 @@ def test_ring_layouts_all_ranks(gpu, W, zigzag, dtype):
         run_full_check(qs, k, v, True, W, zigzag, r, f"W={W} zigzag={zigzag} rank={r}")
 
 
+@pytest.mark.parametrize("fused_merge", [True, False])
 @pytest.mark.parametrize("W,zigzag", [(2, False), (3, True), (4, True)])
-def test_ring_steps_equal_oracle(gpu, W, zigzag):
+def test_ring_steps_equal_oracle(gpu, W, zigzag, fused_merge):
     N = 2 * W * 96 if zigzag else W * 160
     q, k, v = workloads.make_qkv(1, N, N, 4, 2, 128, torch.bfloat16, seed=5 + W)
     dev = torch.device("cuda:0")
@@ -214,7 +220,8 @@ def test_ring_steps_equal_oracle(gpu, W, zigzag):
     ks = [ring.shard(kd, W, zigzag, r) for r in range(W)]
     vs = [ring.shard(vd, W, zigzag, r) for r in range(W)]
     for r in range(W):
-        out, lse = ring.ring_forward_steps(ring.shard(qd, W, zigzag, r), ks, vs, W, zigzag, r)
+        out, lse = ring.ring_forward_steps(ring.shard(qd, W, zigzag, r), ks, vs, W, zigzag, r,
+                                           fused_merge=fused_merge)
         torch.cuda.synchronize()
         qs = ring.shard(q, W, zigzag, r)
         ref_o, ref_l = oracle.attention(qs, k, v, causal=True,
@@ -401,6 +408,36 @@ def test_split_kv_one_split_is_fwd(gpu):
     a, la = binding.fwd(q, k, v, causal=True)
     b, lb = binding.fwd_split(q, k, v, causal=True, n_splits=1)
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 16), (torch.float16, 64),
+                                     (torch.bfloat16, 128)])
+def test_step_merge_into_rows(gpu, dtype, d):
+    """rattn_fwd_step_merge on a row range of a batched output: rows of batch
+    b sit Nq_out apart, so the kernel addresses them from out_rows/row_off."""
+    dev = torch.device("cuda:0")
+    B, Nq_out, off, Nq, Nk = 2, 400, 150, 200, 300
+    q, k, v = workloads.make_qkv(B, Nq, Nk, 4, 2, d, dtype, seed=80 + d)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    # running result: the first 100 keys as a step of its own, written into
+    # rows [off, off + Nq) of a larger float32 output that starts out garbage
+    # elsewhere; queries at positions 1000.. see every key (causal passes)
+    out = torch.full((B, Nq_out, 4, d), 7.0, device=dev)
+    lse = torch.full((B, Nq_out, 4), 3.0, device=dev)
+    o1, l1 = binding.fwd_step(qd, kd[:, :100].contiguous(), vd[:, :100].contiguous(), True,
+                              [(1000, Nq)], [(0, 100)])
+    out[:, off:off + Nq] = o1
+    lse[:, off:off + Nq] = l1
+    binding.fwd_step_merge(qd, kd[:, 100:].contiguous(), vd[:, 100:].contiguous(), True,
+                           [(1000, Nq)], [(100, Nk - 100)], out, lse, row_off=off)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention(q, k, v, causal=True, q_pos=np.arange(1000, 1000 + Nq),
+                                    k_pos=np.arange(Nk))
+    compare(host(out[:, off:off + Nq]), host(lse[:, off:off + Nq]), ref_o, ref_l, dtype,
+            what=f"step merge {dtype} d={d}")
+    # rows outside the range are untouched
+    assert (out[:, :off] == 7.0).all() and (out[:, off + Nq:] == 7.0).all()
+    assert (lse[:, :off] == 3.0).all() and (lse[:, off + Nq:] == 3.0).all()
 
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
