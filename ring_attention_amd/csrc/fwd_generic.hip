@@ -11,8 +11,8 @@
 // Scores are exponentiated as exp2(s*scale*log2(e) - m) with m kept in that
 // scaled base-2 unit.  For 16-bit inputs p is rounded to the input type before
 // it multiplies V, as the Triton kernel of the yz520gzy chapter does; l keeps
-// the unrounded p.  This kernel carries the float32 path; the MFMA kernel
-// carries the 16-bit inputs for d >= 32.
+// the unrounded p.  This kernel carries the float32 path; the MFMA kernels
+// carry every 16-bit case (the 16-bit branches here are kept for completeness).
 #include "kcommon.h"
 
 namespace rattn {

@@ -11,7 +11,9 @@
 // same chapter casts p to v's type before the second dot).
 //
 // How, on CDNA4:
-//   * A workgroup of 4 wavefronts owns a tile of 128 query rows, 32 per wave.
+//   * A workgroup of 4 wavefronts owns a tile of 128 query rows, 32 per wave;
+//     d = 16, 32 or 64 (at d = 16 the V^T operand is padded to 32 rows with
+//     zeros and only O^T rows 0..15 are stored).
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{bf16,f16}: A = 32 keys x 16 dims read from LDS,
 //     B = 16 dims x 32 queries held in registers for the whole tile.  In the
@@ -58,14 +60,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   constexpr int KP = D + 8;    // K row pitch in LDS (elements)
   constexpr int VP = kBc + 8;  // V^T row pitch in LDS (elements)
   constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int CH = kBc * CPR / kThreads;  // chunks per thread per tensor
+  constexpr int NCH = kBc * CPR;  // 16-byte chunks per tile per tensor
+  constexpr int CH = (NCH + kThreads - 1) / kThreads;  // chunks per thread per tensor
   constexpr int KS = D / 16;   // MFMA k-steps for S
-  constexpr int DB = D / 32;   // 32-row blocks of O^T
-  static_assert(CH >= 1 && (kBc * CPR) % kThreads == 0, "tile/thread mismatch");
+  // 32-row blocks of O^T; at d = 16 one block whose rows 16..31 are zero
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  constexpr int VROWS = 32 * DB;  // rows of V^T in LDS (>= D)
+  static_assert(NCH % kThreads == 0 || NCH < kThreads, "tile/thread mismatch");
 
   // 16-bit patterns in LDS; read back as MFMA operand vectors.
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBc * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][VROWS * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   int krow_of[CH], vrow_of[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int ci = tid + kThreads * i;
+    const int ci = (tid + kThreads * i) % NCH;  // threads past NCH repeat a chunk
     krow_of[i] = ci / CPR;
     vrow_of[i] = ci % kBc;
     koff[i] = (uint32_t)((krow_of[i] * kv_stride + (ci % CPR) * 8) * sizeof(E));
@@ -167,6 +172,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int ci = tid + kThreads * i;
+      if (NCH < kThreads && ci >= NCH) continue;
       const int kr = ci / CPR, kc = ci % CPR;
       *(uint4*)&k_lds[buf][kr * KP + kc * 8] = kreg[i];
       const int vr = ci % kBc, vc = ci / kBc;
@@ -178,6 +184,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
     }
   };
 
+  if (VROWS > D) {
+    // d = 16: V^T rows D .. 31 of both buffers stay zero (O^T rows 16..31 = 0)
+    for (int i = tid; i < 2 * (VROWS - D) * VP; i += kThreads)
+      vt_lds[i / ((VROWS - D) * VP)][D * VP + i % ((VROWS - D) * VP)] = 0;
+  }
   int64_t left;  // key tiles of this split still to visit
   TileCursor cur = split_cursor<kBc>(s, qt.rank, qhi, wi.split, p.n_splits, &left);
   if (left > 0) {
@@ -287,6 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      if (32 * db + 8 * j >= D) continue;  // d = 16: only O^T rows 0..15 exist
       const int d0 = 32 * db + 8 * j + 4 * hl;
       if (OUT_F32) {
         f32x4 o4;
@@ -324,6 +336,7 @@ template <typename TT>
 hipError_t launch_d(int d, const void* q, const void* k, const void* v, void* out, float* lse,
                     bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
   switch (d) {
+    case 16: return launch_t<TT, 16>(q, k, v, out, lse, out_f32, p, s, stream);
     case 32: return launch_t<TT, 32>(q, k, v, out, lse, out_f32, p, s, stream);
     case 64: return launch_t<TT, 64>(q, k, v, out, lse, out_f32, p, s, stream);
     default: return hipErrorInvalidValue;

@@ -62,7 +62,7 @@ int check_dtype_d(int dtype, int d) {
   return RATTN_OK;
 }
 
-bool use_mfma(int dtype, int d) { return dtype != RATTN_F32 && d >= 32; }
+bool use_mfma(int dtype, int d) { return dtype != RATTN_F32 && d >= 16; }
 
 // Query rows per tile of the kernel that will run (the schedule is built for it).
 int tile_rows(int dtype, int d) {
