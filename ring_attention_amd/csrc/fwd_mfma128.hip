@@ -21,7 +21,8 @@
 // Every M phase runs the same 32-MFMA stream (a single code path keeps the
 // accumulators in place); a tile a wave does not score gets P = 0.  The
 // stream reads each MFMA's LDS operand a few MFMAs ahead.  Scalar
-// bookkeeping and DMA issue sit in the V phase, next to the VALU work.
+// bookkeeping sits in the V phase, next to the VALU work; each M phase
+// opens by issuing this wave's share of the DMA of a later tile.
 //
 // Data path.  K and V tiles (64 keys x 128 dims) move global -> LDS by
 // direct-to-LDS DMA into a ring of 4 buffers; tile k is requested three or
