@@ -5,8 +5,11 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 never imports it, and it imports nothing from the HIP path.
 
 Contents
-  oracle.c        the definition softmax(scale*QK^T)V in double (C + OpenMP)
-  __init__.py     ctypes wrapper: ``attention``, ``merge``, ``build``
+  oracle.c        the definition softmax(scale*QK^T)V in double (C + OpenMP),
+                  and its gradients dQ, dK, dV (backward pass)
+  __init__.py     ctypes wrapper: ``attention``, ``merge``, ``attention_bwd``
+                  (with ``bwd_stats``, ``bwd_dq``, ``bwd_dkv`` for sampled
+                  rows), ``build``
   layouts.py      global positions of query/key rows under the ring layouts
                   (contiguous blocks, ZigZag chunk pairs) and the per-step plan
                   of the ZigZag ring
@@ -64,6 +67,17 @@ def _load(path: str | None = None):
     lib.oracle_merge_rows.restype = ctypes.c_int
     lib.oracle_merge_rows.argtypes = [f64p, f64p, f64p, f64p, ctypes.c_int64,
                                       ctypes.c_int, f64p, f64p]
+    bwd_head = [ctypes.c_void_p] * 4 + [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int, i64p, i64p, ctypes.c_int, ctypes.c_double]
+    lib.oracle_bwd_stats.restype = ctypes.c_int
+    lib.oracle_bwd_stats.argtypes = bwd_head + [ctypes.c_int64, i64p, f64p, f64p, ctypes.c_int]
+    lib.oracle_bwd_dq.restype = ctypes.c_int
+    lib.oracle_bwd_dq.argtypes = bwd_head + [f64p, f64p, ctypes.c_int64, i64p, f64p,
+                                             ctypes.c_int]
+    lib.oracle_bwd_dkv.restype = ctypes.c_int
+    lib.oracle_bwd_dkv.argtypes = bwd_head + [f64p, f64p, ctypes.c_int64, i64p, f64p, f64p,
+                                              ctypes.c_int]
     lib.oracle_f16_to_double.restype = ctypes.c_double
     lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = ctypes.c_double
@@ -191,6 +205,123 @@ def merge(o_a, l_a, o_b, l_b, lib_path: str | None = None):
     if rc != 0:
         raise ValueError("oracle_merge_rows rejected its arguments")
     return o, lse
+
+
+class _BwdArgs:
+    """Storage views, shapes and positions shared by the backward wrappers."""
+
+    def __init__(self, q, k, v, dout, causal, scale, q_pos, k_pos):
+        self.qs, dt = _as_storage(q)
+        self.ks, dtk = _as_storage(k)
+        self.vs, dtv = _as_storage(v)
+        self.ds, dtd = _as_storage(dout)
+        if not (dt == dtk == dtv == dtd):
+            raise TypeError("oracle: q, k, v, dout must share one dtype")
+        if self.qs.ndim != 4 or self.ks.shape != self.vs.shape or self.ds.shape != self.qs.shape:
+            raise ValueError("oracle: q, dout [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d]")
+        self.dtype = dt
+        self.B, self.Nq, self.Hq, self.d = self.qs.shape
+        _, self.Nk, self.Hkv, _ = self.ks.shape
+        if self.ks.shape[0] != self.B or self.ks.shape[3] != self.d:
+            raise ValueError("oracle: shape mismatch")
+        self.scale = 1.0 / np.sqrt(self.d) if scale is None else float(scale)
+        self.qp = _i64(np.arange(self.Nq) if q_pos is None else q_pos)
+        self.kp = _i64(np.arange(self.Nk) if k_pos is None else k_pos)
+        if self.qp.shape != (self.Nq,) or self.kp.shape != (self.Nk,):
+            raise ValueError("oracle: position arrays must have one entry per row")
+        self.causal = int(bool(causal))
+
+    def head(self):
+        return (self.qs.ctypes.data, self.ks.ctypes.data, self.vs.ctypes.data,
+                self.ds.ctypes.data, self.dtype, self.B, self.Hq, self.Hkv, self.Nq, self.Nk,
+                self.d, _ptr(self.qp, ctypes.c_int64), _ptr(self.kp, ctypes.c_int64),
+                self.causal, self.scale)
+
+
+def _rows(rows, n_all):
+    if rows is None:
+        return None, n_all
+    r = _i64(rows).reshape(-1, 3)
+    return r, r.shape[0]
+
+
+def bwd_stats(q, k, v, dout, causal=False, scale=None, q_pos=None, k_pos=None, rows=None,
+              n_threads=None, lib_path=None):
+    """Per query row: LSE and D = dO . O (float64).  rows: optional (n, 3)
+    (b, i, hq) triples; returns (lse, delta) of shape [n] or [B, Nq, Hq]."""
+    lib = _load(lib_path)
+    a = _BwdArgs(q, k, v, dout, causal, scale, q_pos, k_pos)
+    r, n = _rows(rows, a.B * a.Nq * a.Hq)
+    lse = np.empty(n, np.float64)
+    delta = np.empty(n, np.float64)
+    f = ctypes.c_double
+    rc = lib.oracle_bwd_stats(*a.head(), n, None if r is None else _ptr(r, ctypes.c_int64),
+                              _ptr(lse, f), _ptr(delta, f), n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_bwd_stats rejected its arguments")
+    if rows is None:
+        return lse.reshape(a.B, a.Nq, a.Hq), delta.reshape(a.B, a.Nq, a.Hq)
+    return lse, delta
+
+
+def bwd_dq(q, k, v, dout, lse_all, delta_all, causal=False, scale=None, q_pos=None,
+           k_pos=None, rows=None, n_threads=None, lib_path=None):
+    """dQ rows (float64).  lse_all, delta_all: [B, Nq, Hq] from ``bwd_stats``
+    (only the requested rows' entries are read).  Returns [n, d] for (b, i, hq)
+    rows, else [B, Nq, Hq, d]."""
+    lib = _load(lib_path)
+    a = _BwdArgs(q, k, v, dout, causal, scale, q_pos, k_pos)
+    la = np.ascontiguousarray(lse_all, np.float64)
+    da = np.ascontiguousarray(delta_all, np.float64)
+    if la.shape != (a.B, a.Nq, a.Hq) or da.shape != la.shape:
+        raise ValueError("oracle.bwd_dq: lse_all / delta_all must be [B, Nq, Hq]")
+    r, n = _rows(rows, a.B * a.Nq * a.Hq)
+    dq = np.empty((n, a.d), np.float64)
+    f = ctypes.c_double
+    rc = lib.oracle_bwd_dq(*a.head(), _ptr(la, f), _ptr(da, f), n,
+                           None if r is None else _ptr(r, ctypes.c_int64), _ptr(dq, f),
+                           n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_bwd_dq rejected its arguments")
+    return dq if rows is not None else dq.reshape(a.B, a.Nq, a.Hq, a.d)
+
+
+def bwd_dkv(q, k, v, dout, lse_all, delta_all, causal=False, scale=None, q_pos=None,
+            k_pos=None, rows=None, n_threads=None, lib_path=None):
+    """dK and dV rows (float64), summed over the query heads of each key/value
+    head's group.  rows: optional (n, 3) (b, j, g) triples.  Returns (dk, dv)
+    of shape [n, d] or [B, Nk, Hkv, d]."""
+    lib = _load(lib_path)
+    a = _BwdArgs(q, k, v, dout, causal, scale, q_pos, k_pos)
+    la = np.ascontiguousarray(lse_all, np.float64)
+    da = np.ascontiguousarray(delta_all, np.float64)
+    if la.shape != (a.B, a.Nq, a.Hq) or da.shape != la.shape:
+        raise ValueError("oracle.bwd_dkv: lse_all / delta_all must be [B, Nq, Hq]")
+    r, n = _rows(rows, a.B * a.Nk * a.Hkv)
+    dk = np.empty((n, a.d), np.float64)
+    dv = np.empty((n, a.d), np.float64)
+    f = ctypes.c_double
+    rc = lib.oracle_bwd_dkv(*a.head(), _ptr(la, f), _ptr(da, f), n,
+                            None if r is None else _ptr(r, ctypes.c_int64), _ptr(dk, f),
+                            _ptr(dv, f), n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_bwd_dkv rejected its arguments")
+    if rows is None:
+        shp = (a.B, a.Nk, a.Hkv, a.d)
+        return dk.reshape(shp), dv.reshape(shp)
+    return dk, dv
+
+
+def attention_bwd(q, k, v, dout, causal=False, scale=None, q_pos=None, k_pos=None,
+                  n_threads=None, lib_path=None):
+    """Gradients of sum(dout * attention(q, k, v)) with respect to q, k, v, in
+    float64: returns (dq [B,Nq,Hq,d], dk, dv [B,Nk,Hkv,d], lse, delta [B,Nq,Hq])."""
+    kw = dict(causal=causal, scale=scale, q_pos=q_pos, k_pos=k_pos, n_threads=n_threads,
+              lib_path=lib_path)
+    lse, delta = bwd_stats(q, k, v, dout, **kw)
+    dq = bwd_dq(q, k, v, dout, lse, delta, **kw)
+    dk, dv = bwd_dkv(q, k, v, dout, lse, delta, **kw)
+    return dq, dk, dv, lse, delta
 
 
 def decode_f16(bits: int) -> float:

@@ -35,7 +35,8 @@
  *   A empty:  O = 0, LSE = -inf.
  *
  * Two passes per row (max, then the weighted sums), everything in double,
- * no blocking.  Inputs are read in their storage type (fp32, fp16 or bf16 bit
+ * no blocking.  The second half of this file holds the gradients of the same
+ * definition (dQ, dK, dV of a loss with upstream gradient dO).  Inputs are read in their storage type (fp32, fp16 or bf16 bit
  * patterns) and converted exactly to double by the decoders below.
  *
  * Layout: q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d], contiguous, row-major
@@ -263,4 +264,281 @@ int oracle_merge_rows(const double *o_a, const double *l_a, const double *o_b,
         l_out[r] = m + log(z);
     }
     return 0;
+}
+
+/*
+ * ---------------------------------------------------------------------------
+ * Gradients of the definition above (backward pass).
+ *
+ * For a loss with upstream gradient dO = dL/dO, differentiating
+ *   O_i = sum_j P_ij v_j,  P_ij = exp(s_ij - LSE_i),  s_ij = scale q_i . k_j
+ * gives (chain rule through the softmax, whose Jacobian row is
+ * P_ij (delta_jl - P_il)):
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = dO_i . O_i              (= sum_j P_ij dP_ij)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale sum_j dS_ij k_j
+ *   dK_j  = scale sum_i dS_ij q_i
+ * with sums over visible pairs only (a masked pair has P = 0).  This is the
+ * recomputation backward of the youngju.dev "Ring Attention" analysis
+ * (ring_attention_backward: P recomputed from the saved LSE, D as the row sum
+ * of dO * O, scale applied to dS) written from the derivative of the plain
+ * definition.  With GQA a key/value head is shared by the query heads of its
+ * group, so dK and dV sum over those heads (a reading: the pages show no GQA
+ * backward).  A query row with no visible key has O = 0 and contributes
+ * nothing.  Everything in double, per row, no blocking.
+ *
+ * dout has the storage dtype of q, k and v.
+ * ---------------------------------------------------------------------------
+ */
+
+/* LSE_i and D_i = dO_i . O_i of one query row, O and LSE from attend_row. */
+static inline __attribute__((always_inline)) void
+bwd_stats_row(const void *q, const void *k, const void *v, const void *dout, const int dtype,
+              int Hq, int Hkv, int64_t Nq, int64_t Nk, int d, const int64_t *q_pos,
+              const int64_t *k_pos, int causal, double scale, int group, int64_t b, int64_t i,
+              int64_t hq, double *s, double *qrow, double *acc, double *o, double *lse_r,
+              double *delta_r)
+{
+    attend_row(q, k, v, dtype, Hq, Hkv, Nq, Nk, d, q_pos, k_pos, causal, scale, group, b, i,
+               hq, s, qrow, acc, o, lse_r);
+    double dsum = 0.0;
+    for (int t = 0; t < d; ++t)
+        dsum += load(dout, ((b * Nq + i) * Hq + hq) * d + t, dtype) * o[t];
+    *delta_r = dsum;
+}
+
+static int bwd_check(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                     int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int d,
+                     const int64_t *q_pos, const int64_t *k_pos, int causal)
+{
+    return !q || !k || !v || !dout || B < 1 || Hq < 1 || Hkv < 1 || d < 1 || Nq < 0 ||
+           Nk < 0 || Hq % Hkv != 0 || (causal && (!q_pos || !k_pos)) || dtype < ORACLE_F32 ||
+           dtype > ORACLE_BF16;
+}
+
+/*
+ * Per query row (b, i, hq): lse = LSE_i and delta = D_i.
+ *   rows : n_rows triples (b, i, hq), or NULL for every row in (b, i, hq)
+ *          row-major order (n_rows must then equal B*Nq*Hq)
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_bwd_stats(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                     int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int d,
+                     const int64_t *q_pos, const int64_t *k_pos, int causal, double scale,
+                     int64_t n_rows, const int64_t *rows, double *lse, double *delta,
+                     int n_threads)
+{
+    if (bwd_check(q, k, v, dout, dtype, B, Hq, Hkv, Nq, Nk, d, q_pos, k_pos, causal) ||
+        !lse || !delta || (!rows && n_rows != (int64_t)B * Nq * Hq))
+        return -1;
+    const int group = Hq / Hkv;
+    int bad = 0;
+    build_luts();
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel reduction(| : bad)
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qrow || !acc || !o) {
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t b, i, hq;
+                if (rows) {
+                    b = rows[3 * r]; i = rows[3 * r + 1]; hq = rows[3 * r + 2];
+                } else {
+                    hq = r % Hq; i = (r / Hq) % Nq; b = r / ((int64_t)Hq * Nq);
+                }
+                if (b < 0 || b >= B || i < 0 || i >= Nq || hq < 0 || hq >= Hq) {
+                    bad = 1;
+                    continue;
+                }
+                switch (dtype) {
+                case ORACLE_F32:
+                    bwd_stats_row(q, k, v, dout, ORACLE_F32, Hq, Hkv, Nq, Nk, d, q_pos, k_pos,
+                                  causal, scale, group, b, i, hq, s, qrow, acc, o, lse + r,
+                                  delta + r);
+                    break;
+                case ORACLE_F16:
+                    bwd_stats_row(q, k, v, dout, ORACLE_F16, Hq, Hkv, Nq, Nk, d, q_pos, k_pos,
+                                  causal, scale, group, b, i, hq, s, qrow, acc, o, lse + r,
+                                  delta + r);
+                    break;
+                default:
+                    bwd_stats_row(q, k, v, dout, ORACLE_BF16, Hq, Hkv, Nq, Nk, d, q_pos, k_pos,
+                                  causal, scale, group, b, i, hq, s, qrow, acc, o, lse + r,
+                                  delta + r);
+                    break;
+                }
+            }
+        }
+        free(s);
+        free(qrow);
+        free(acc);
+        free(o);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * dQ rows.  lse_all, delta_all: [B, Nq, Hq] from oracle_bwd_stats (only the
+ * entries of the requested rows are read).  rows as in oracle_bwd_stats;
+ * dq: [n_rows, d].
+ */
+int oracle_bwd_dq(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                  int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int d,
+                  const int64_t *q_pos, const int64_t *k_pos, int causal, double scale,
+                  const double *lse_all, const double *delta_all, int64_t n_rows,
+                  const int64_t *rows, double *dq, int n_threads)
+{
+    if (bwd_check(q, k, v, dout, dtype, B, Hq, Hkv, Nq, Nk, d, q_pos, k_pos, causal) ||
+        !lse_all || !delta_all || !dq || (!rows && n_rows != (int64_t)B * Nq * Hq))
+        return -1;
+    const int group = Hq / Hkv;
+    int bad = 0;
+    build_luts();
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel reduction(| : bad)
+    {
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *dorow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!qrow || !dorow) {
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t b, i, hq;
+                if (rows) {
+                    b = rows[3 * r]; i = rows[3 * r + 1]; hq = rows[3 * r + 2];
+                } else {
+                    hq = r % Hq; i = (r / Hq) % Nq; b = r / ((int64_t)Hq * Nq);
+                }
+                double *g_out = dq + r * d;
+                for (int t = 0; t < d; ++t) g_out[t] = 0.0;
+                if (b < 0 || b >= B || i < 0 || i >= Nq || hq < 0 || hq >= Hq) {
+                    bad = 1;
+                    continue;
+                }
+                const int64_t row = (b * Nq + i) * Hq + hq;
+                const double L = lse_all[row], Dl = delta_all[row];
+                if (L == -INFINITY) continue;   /* nothing visible: O = 0 */
+                const int64_t g = hq / group;
+                for (int t = 0; t < d; ++t) {
+                    qrow[t] = load(q, row * d + t, dtype);
+                    dorow[t] = load(dout, row * d + t, dtype);
+                }
+                for (int64_t j = 0; j < Nk; ++j) {
+                    if (causal && k_pos[j] > q_pos[i]) continue;
+                    const int64_t kb = ((b * Nk + j) * Hkv + g) * d;
+                    double dot = 0.0, dp = 0.0;
+                    for (int t = 0; t < d; ++t) {
+                        dot += qrow[t] * load(k, kb + t, dtype);
+                        dp += dorow[t] * load(v, kb + t, dtype);
+                    }
+                    const double P = exp(scale * dot - L);
+                    const double dS = P * (dp - Dl);
+                    for (int t = 0; t < d; ++t) g_out[t] += dS * load(k, kb + t, dtype);
+                }
+                for (int t = 0; t < d; ++t) g_out[t] *= scale;
+            }
+        }
+        free(qrow);
+        free(dorow);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * dK and dV rows of key/value head rows (b, j, g): sums over the query heads
+ * g*group .. g*group+group-1 and every query row that sees key j.
+ *   rows : n_rows triples (b, j, g), or NULL for every row in (b, j, g)
+ *          row-major order (n_rows must then equal B*Nk*Hkv)
+ *   lse_all, delta_all: [B, Nq, Hq] (the rows of the group's heads are read)
+ *   dk, dv: [n_rows, d]
+ */
+int oracle_bwd_dkv(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                   int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int d,
+                   const int64_t *q_pos, const int64_t *k_pos, int causal, double scale,
+                   const double *lse_all, const double *delta_all, int64_t n_rows,
+                   const int64_t *rows, double *dk, double *dv, int n_threads)
+{
+    if (bwd_check(q, k, v, dout, dtype, B, Hq, Hkv, Nq, Nk, d, q_pos, k_pos, causal) ||
+        !lse_all || !delta_all || !dk || !dv || (!rows && n_rows != (int64_t)B * Nk * Hkv))
+        return -1;
+    const int group = Hq / Hkv;
+    int bad = 0;
+    build_luts();
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel reduction(| : bad)
+    {
+        double *krow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *vrow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!krow || !vrow) {
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t b, j, g;
+                if (rows) {
+                    b = rows[3 * r]; j = rows[3 * r + 1]; g = rows[3 * r + 2];
+                } else {
+                    g = r % Hkv; j = (r / Hkv) % Nk; b = r / ((int64_t)Hkv * Nk);
+                }
+                double *gk = dk + r * d, *gv = dv + r * d;
+                for (int t = 0; t < d; ++t) gk[t] = gv[t] = 0.0;
+                if (b < 0 || b >= B || j < 0 || j >= Nk || g < 0 || g >= Hkv) {
+                    bad = 1;
+                    continue;
+                }
+                const int64_t kb = ((b * Nk + j) * Hkv + g) * d;
+                for (int t = 0; t < d; ++t) {
+                    krow[t] = load(k, kb + t, dtype);
+                    vrow[t] = load(v, kb + t, dtype);
+                }
+                for (int64_t hq = g * group; hq < (g + 1) * group; ++hq) {
+                    for (int64_t i = 0; i < Nq; ++i) {
+                        if (causal && k_pos[j] > q_pos[i]) continue;
+                        const int64_t row = (b * Nq + i) * Hq + hq;
+                        const double L = lse_all[row], Dl = delta_all[row];
+                        if (L == -INFINITY) continue;
+                        double dot = 0.0, dp = 0.0;
+                        for (int t = 0; t < d; ++t) {
+                            dot += load(q, row * d + t, dtype) * krow[t];
+                            dp += load(dout, row * d + t, dtype) * vrow[t];
+                        }
+                        const double P = exp(scale * dot - L);
+                        const double dS = P * (dp - Dl);
+                        for (int t = 0; t < d; ++t) {
+                            gk[t] += dS * load(q, row * d + t, dtype);
+                            gv[t] += P * load(dout, row * d + t, dtype);
+                        }
+                    }
+                }
+                for (int t = 0; t < d; ++t) gk[t] *= scale;
+            }
+        }
+        free(krow);
+        free(vrow);
+    }
+    return bad ? -1 : 0;
 }

@@ -201,3 +201,44 @@ def online_softmax_over_blocks(q, k_blocks, v_blocks, scale: float | None = None
         l = l + p.sum(axis=1)
         m = m_new
     return o / l[:, None], m + np.log(l)
+
+
+def ring_backward(q, k, v, o, lse, do, W: int, rank: int, scale: float | None = None):
+    """The ring backward of one device, simulated: gradients of the device's
+    query block and of every key/value block, non-causal.
+
+    Follows the youngju.dev ``ring_attention_backward`` description: the
+    device first forms D = rowsum(dO * O) from its saved output; then at each
+    of the W steps it holds the key/value block of device (rank - step) mod W,
+    recomputes S = scale Q K^T and P = exp(S - lse) from the saved log-sum-exp,
+    and forms dV_blk = P^T dO, dP = dO V^T, dS = P (dP - D) scale,
+    dQ += dS K, dK_blk = dS^T Q.  The block gradients go back to the block's
+    owner, which sums what every device sends it.
+
+    q, o, do: [Nq, d] (this device's query block), lse [Nq]; k, v: [Nk, d]
+    (the whole sequence, W equal blocks).  Returns (dQ [Nq, d], dK, dV [Nk, d])
+    where dK, dV hold this device's contribution to every block.
+    """
+    q, k, v, o, do = (np.asarray(x, np.float64) for x in (q, k, v, o, do))
+    lse = np.asarray(lse, np.float64)
+    Nk, d = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if Nk % W:
+        raise ValueError("Nk must be a multiple of W")
+    S_blk = Nk // W
+    D = (do * o).sum(axis=1, keepdims=True)
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for step in range(W):
+        src = (rank - step) % W
+        rows = slice(src * S_blk, (src + 1) * S_blk)
+        Kb, Vb = k[rows], v[rows]
+        P = _exp_shift((q @ Kb.T) * scale, lse[:, None])
+        dV[rows] += P.T @ do
+        dP = do @ Vb.T
+        dS = P * (dP - D) * scale
+        dQ += dS @ Kb
+        dK[rows] += dS.T @ q
+    return dQ, dK, dV
