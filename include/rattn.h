@@ -1,5 +1,6 @@
 /*
- * rattn.h -- C ABI of the MI355X (gfx950) exact ring-attention forward.
+ * rattn.h -- C ABI of the MI355X (gfx950) exact ring attention: the forward
+ * and its backward.
  *
  * The operation is exact attention, softmax(scale * Q K^T) V (guijiagi.com
  * "ring-attention-explained", memory-wall section, first formula), computed
@@ -156,6 +157,70 @@ RATTN_API int rattn_fwd_split(const void* q, const void* k, const void* v, void*
  */
 RATTN_API int rattn_split_hint(int B, int Hq, int64_t Nq, int64_t N, int d, int dtype,
                                int n_ring_steps, int zigzag, int rank, int n_cu);
+
+/*
+ * ---- Backward ----------------------------------------------------------
+ * Gradients of sum(dout * out) with respect to q, k and v, recomputing the
+ * probabilities from the forward's lse (youngju.dev "Ring Attention"
+ * analysis, ring_attention_backward):
+ *   P_ij = exp(scale q_i.k_j - lse_i)  (0 when key j is not visible to row i)
+ *   D_i  = rowsum(dout_i * out_i)
+ *   dv_j = sum_i P_ij dout_i
+ *   dS_ij = P_ij (dout_i . v_j - D_i)
+ *   dq_i = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i
+ * With GQA, dk and dv of a key/value head sum over the query heads of its
+ * group.  A row whose lse is -inf (it saw no key) contributes nothing.
+ */
+
+/*
+ * D = rowsum(dout * out) for `rows` rows of d elements: out, dout of
+ * dtype, contiguous [rows, d] (e.g. [B, Nq, Hq, d] with rows = B*Nq*Hq);
+ * delta float32 [rows].  Pointers 16-byte aligned (delta 4-byte).
+ */
+RATTN_API int rattn_bwd_delta(const void* out, const void* dout, float* delta, int64_t rows,
+                              int d, int dtype, void* stream);
+
+/*
+ * Backward of rattn_fwd, same layout arguments (B, Hq, Hkv, Nq, N, d, dtype,
+ * scale, causal, n_ring_steps, zigzag, rank).
+ *   q, out, dout [B, Nq, Hq, d] dtype; lse [B, Nq, Hq] float32 from rattn_fwd;
+ *   k, v [B, N, Hkv, d] dtype.
+ *   dq [B, Nq, Hq, d], dk, dv [B, N, Hkv, d] in dtype: written (not added to).
+ *   delta_ws: caller scratch of B*Nq*Hq float32 (receives D).
+ * With rank >= 0 the queries are device r's shard, and dk/dv are that
+ * device's contribution to every key/value row (what the ring sends back to
+ * each block's owner); with rank = -1 they are the full gradients.  The
+ * result does not depend on the ring order.  All tensor pointers 16-byte
+ * aligned; outputs must not overlap the inputs.
+ */
+RATTN_API int rattn_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        float* delta_ws, int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d,
+                        int dtype, float scale, int causal, int n_ring_steps, int zigzag,
+                        int rank, void* stream);
+
+/*
+ * One ring step of the backward: the pairs between query rows
+ * [q_off, q_off + Nq) of a [B, q_rows, Hq, .] row space (q, dout dtype
+ * [.., d]; lse, delta float32 [B, q_rows, Hq]; dq_acc float32 [.., d]) and
+ * key/value rows [k_off, k_off + Nk) of a [B, k_rows, Hkv, d] row space
+ * (k, v dtype; dk_acc, dv_acc float32).  The step's contributions are ADDED
+ * to dq_acc, dk_acc and dv_acc (float32 accumulators the caller zeroes
+ * once).  Positions as rattn_fwd_step: query row q_off + i sits at
+ * q_seg_start[0] + i for i < q_seg_len[0], else at
+ * q_seg_start[1] + (i - q_seg_len[0]); keys likewise (HOST arrays of two
+ * int64, lengths summing to Nq and Nk).  lse and delta are those of the
+ * final forward result (rattn_fwd or the merged ring steps) and
+ * rattn_bwd_delta.  Accumulators must not overlap the inputs; calls that
+ * add to the same accumulator rows must be ordered on one stream.
+ */
+RATTN_API int rattn_bwd_step(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, const float* delta, float* dq_acc, float* dk_acc,
+                             float* dv_acc, int B, int Hq, int Hkv, int64_t q_rows,
+                             int64_t q_off, int64_t Nq, int64_t k_rows, int64_t k_off,
+                             int64_t Nk, int d, int dtype, float scale, int causal,
+                             const int64_t* q_seg_start, const int64_t* q_seg_len,
+                             const int64_t* k_seg_start, const int64_t* k_seg_len, void* stream);
 
 /* Static description of a status code; never NULL. */
 RATTN_API const char* rattn_status_string(int status);

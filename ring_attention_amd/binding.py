@@ -21,7 +21,8 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # Exported symbols, in the order include/rattn.h declares them.
 EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_fwd_step_merge", "rattn_merge",
-           "rattn_fwd_split", "rattn_split_hint", "rattn_status_string")
+           "rattn_fwd_split", "rattn_split_hint", "rattn_bwd_delta", "rattn_bwd",
+           "rattn_bwd_step", "rattn_status_string")
 
 
 class RattnError(RuntimeError):
@@ -62,6 +63,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                     i32, i32, i32, i32, i32, vp, i64, vp]
     lib.rattn_split_hint.restype = i32
     lib.rattn_split_hint.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32]
+    lib.rattn_bwd_delta.restype = i32
+    lib.rattn_bwd_delta.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    lib.rattn_bwd.restype = i32
+    lib.rattn_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i64, i64, i32, i32, f32, i32, i32, i32,
+                                          i32, vp]
+    lib.rattn_bwd_step.restype = i32
+    lib.rattn_bwd_step.argtypes = [vp] * 9 + [i32, i32, i32, i64, i64, i64, i64, i64, i64, i32,
+                                              i32, f32, i32, i64p, i64p, i64p, i64p, vp]
     lib.rattn_status_string.restype = ctypes.c_char_p
     lib.rattn_status_string.argtypes = [i32]
     if path is None:
@@ -249,3 +258,103 @@ def merge(out: torch.Tensor, lse: torch.Tensor, blk_out: torch.Tensor, blk_lse: 
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def _like(name, t, ref, dtype=None):
+    """t must be a contiguous tensor on ref's device, of dtype (default: ref's)."""
+    want = ref.dtype if dtype is None else dtype
+    if not isinstance(t, torch.Tensor) or t.dtype != want or not t.is_contiguous() or \
+            t.device != ref.device:
+        raise ValueError(f"{name} must be a contiguous {want} tensor on {ref.device}")
+
+
+def bwd_delta(out: torch.Tensor, dout: torch.Tensor, delta: torch.Tensor | None = None):
+    """D = rowsum(dout * out) over the last dim (rattn_bwd_delta), float32."""
+    _like("dout", dout, out)
+    if out.dtype not in DTYPE_CODES or dout.shape != out.shape or not out.is_cuda:
+        raise ValueError("out and dout must be matching GPU tensors")
+    d = out.shape[-1]
+    rows = out.numel() // d if d else 0
+    if delta is None:
+        delta = torch.empty(out.shape[:-1], dtype=torch.float32, device=out.device)
+    _like("delta", delta, out, torch.float32)
+    if delta.numel() != rows:
+        raise ValueError("delta must hold one value per row")
+    rc = load_library().rattn_bwd_delta(out.data_ptr(), dout.data_ptr(), delta.data_ptr(), rows,
+                                        d, DTYPE_CODES[out.dtype], _stream(out))
+    _check("rattn_bwd_delta", rc)
+    return delta
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+        lse: torch.Tensor, dout: torch.Tensor, causal: bool = False, n_ring_steps: int = 1,
+        zigzag: bool = False, rank: int = -1, scale: float | None = None,
+        dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+        dv: torch.Tensor | None = None, delta_ws: torch.Tensor | None = None):
+    """Backward of ``fwd`` (rattn_bwd): returns (dq, dk, dv) in q's dtype.
+
+    out, lse: the forward's results; dout: the gradient of the loss with
+    respect to out.  Layout arguments as ``fwd``."""
+    _qkv(q, k, v)
+    B, Nq, Hq, d = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    _like("out", out, q)
+    _like("dout", dout, q)
+    _like("lse", lse, q, torch.float32)
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Nq, Hq):
+        raise ValueError("out, dout must be [B, Nq, Hq, d] and lse [B, Nq, Hq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta_ws is None:
+        delta_ws = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _like(name, t, ref)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have the shape of its input")
+    _like("delta_ws", delta_ws, q, torch.float32)
+    if delta_ws.numel() < B * Nq * Hq:
+        raise ValueError("delta_ws must hold B*Nq*Hq floats")
+    rc = load_library().rattn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta_ws.data_ptr(),
+        B, Hq, Hkv, Nq, N, d, DTYPE_CODES[q.dtype], _scale(scale), int(bool(causal)),
+        int(n_ring_steps), int(bool(zigzag)), int(rank), _stream(q))
+    _check("rattn_bwd", rc)
+    return dq, dk, dv
+
+
+def bwd_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+             lse: torch.Tensor, delta: torch.Tensor, dq_acc: torch.Tensor,
+             dk_acc: torch.Tensor, dv_acc: torch.Tensor, causal: bool, q_segs, k_segs,
+             q_off: int = 0, Nq: int | None = None, k_off: int = 0, Nk: int | None = None,
+             scale: float | None = None):
+    """One backward ring step (rattn_bwd_step): adds the contributions of the
+    pairs between query rows [q_off, q_off+Nq) of q and key rows
+    [k_off, k_off+Nk) of k/v to the float32 accumulators dq_acc (q's shape),
+    dk_acc and dv_acc (k's shape).  q_segs / k_segs: up to two
+    (start_position, length) pairs covering those rows in order."""
+    _qkv(q, k, v)
+    B, q_rows, Hq, d = q.shape
+    k_rows, Hkv = k.shape[1], k.shape[2]
+    Nq = q_rows - q_off if Nq is None else Nq
+    Nk = k_rows - k_off if Nk is None else Nk
+    _like("dout", dout, q)
+    for name, t in (("lse", lse), ("delta", delta)):
+        _like(name, t, q, torch.float32)
+        if t.shape != (B, q_rows, Hq):
+            raise ValueError(f"{name} must be [B, Nq, Hq]")
+    for name, t, ref in (("dq_acc", dq_acc, q), ("dk_acc", dk_acc, k), ("dv_acc", dv_acc, v)):
+        _like(name, t, ref, torch.float32)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have the shape of its input")
+    qs, ql = _segs(q_segs)
+    kst, kl = _segs(k_segs)
+    rc = load_library().rattn_bwd_step(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        delta.data_ptr(), dq_acc.data_ptr(), dk_acc.data_ptr(), dv_acc.data_ptr(), B, Hq, Hkv,
+        q_rows, int(q_off), int(Nq), k_rows, int(k_off), int(Nk), d, DTYPE_CODES[q.dtype],
+        _scale(scale), int(bool(causal)), qs, ql, kst, kl, _stream(q))
+    _check("rattn_bwd_step", rc)
+    return dq_acc, dk_acc, dv_acc
+

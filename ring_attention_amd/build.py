@@ -22,7 +22,8 @@ OBJ = os.path.join(ROOT, "_build", "rattn")
 LIB = os.path.join(PKG, "librattn.so")
 ARCH = os.environ.get("RATTN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["rattn_abi.hip", "fwd_generic.hip", "fwd_mfma.hip", "fwd_mfma128.hip", "merge.hip"]
+SOURCES = ["rattn_abi.hip", "fwd_generic.hip", "fwd_mfma.hip", "fwd_mfma128.hip", "merge.hip",
+           "bwd_generic.hip"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

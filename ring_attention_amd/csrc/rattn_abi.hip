@@ -6,6 +6,7 @@
 
 #include <algorithm>
 
+#include "bwd.h"
 #include "launch.h"
 #include "rattn.h"
 #include "ring_sched.h"
@@ -327,6 +328,160 @@ extern "C" int rattn_merge(float* out, float* lse, const float* blk_out, const f
   hipError_t e = launch_merge(out, lse, blk_out, blk_lse, B, H, Nq, Nb, row_off, d,
                               (hipStream_t)stream);
   return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+}
+
+// ---- backward ------------------------------------------------------------
+
+namespace rattn {
+namespace {
+
+BwdParams make_bwd_params(int B, int Hq, int Hkv, float scale) {
+  BwdParams p;
+  memset(&p, 0, sizeof p);
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.group = Hq / Hkv;
+  p.scale = scale;
+  p.c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  return p;
+}
+
+// Keep the non-empty runs (a run of length 0 contributes nothing).
+void set_runs(BwdRun* dst, int32_t* n, const BwdRun* src, int m) {
+  *n = 0;
+  for (int i = 0; i < m; ++i)
+    if (src[i].len > 0) dst[(*n)++] = src[i];
+}
+
+int bwd_dispatch(int dtype, int d, const void* q, const void* k, const void* v,
+                 const void* dout, const float* lse, const float* delta, void* dq, void* dk,
+                 void* dv, const BwdParams& p, void* stream) {
+  const int64_t g1 = bwd_tiles(p.q, p.nq, 64) * p.B * p.Hq;
+  const int64_t g2 = bwd_tiles(p.k, p.nk, 64) * p.B * p.Hkv;
+  if (g1 > INT32_MAX || g2 > INT32_MAX) return RATTN_EUNSUPPORTED;
+  hipError_t e = launch_bwd_generic(dtype, d, q, k, v, dout, lse, delta, dq, dk, dv, p,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+}
+
+}  // namespace
+}  // namespace rattn
+
+extern "C" int rattn_bwd_delta(const void* out, const void* dout, float* delta, int64_t rows,
+                               int d, int dtype, void* stream) {
+  using namespace rattn;
+  if (rows < 0) return RATTN_EINVAL;
+  int rc = check_dtype_d(dtype, d);
+  if (rc != RATTN_OK) return rc;
+  if (rows == 0) return RATTN_OK;
+  if (!out || !dout || !delta) return RATTN_EINVAL;
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(delta, 4)) return RATTN_EINVAL;
+  if (!tensor_ok(1, rows, 1, d) || rows * d / 4 / 256 + 1 > INT32_MAX) return RATTN_EUNSUPPORTED;
+  hipError_t e = launch_bwd_delta(dtype, d, out, dout, delta, rows, (hipStream_t)stream);
+  return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+}
+
+extern "C" int rattn_bwd(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         float* delta_ws, int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d,
+                         int dtype, float scale, int causal, int n_ring_steps, int zigzag,
+                         int rank, void* stream) {
+  using namespace rattn;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
+  if (N < 0 || Nq < 0) return RATTN_EINVAL;
+  if ((Nq > 0 && (!q || !out || !lse || !dout || !dq || !delta_ws)) ||
+      (N > 0 && (!k || !v || !dk || !dv)))
+    return RATTN_EINVAL;
+  int rc = check_dtype_d(dtype, d);
+  if (rc != RATTN_OK) return rc;
+  if ((causal != 0 && causal != 1) || (zigzag != 0 && zigzag != 1)) return RATTN_EINVAL;
+  if (n_ring_steps < 1) return RATTN_EINVAL;
+  if (n_ring_steps > kMaxQSeg / 2) return RATTN_EUNSUPPORTED;
+  const int64_t W = n_ring_steps;
+  const int64_t parts = zigzag ? 2 * W : W;
+  if (N % parts != 0) return RATTN_EINVAL;
+  if (rank < -1 || rank >= W) return RATTN_EINVAL;
+  if (rank == -1 ? Nq != N : Nq != N / W) return RATTN_EINVAL;
+  const void* p16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* x : p16)
+    if (!aligned(x, 16)) return RATTN_EINVAL;
+  if (!aligned(lse, 4) || !aligned(delta_ws, 4)) return RATTN_EINVAL;
+  if (!tensor_ok(B, N, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
+
+  BwdParams p = make_bwd_params(B, Hq, Hkv, resolve_scale(scale, d));
+  p.causal = causal;
+  p.q_rows = Nq;
+  p.k_rows = N;
+  // query runs: the positions of the rows q holds (the gradient does not
+  // depend on the order the ring visits the key/value blocks in)
+  BwdRun qr[2] = {BwdRun{0, Nq, 0}, BwdRun{0, 0, 0}};
+  if (rank >= 0 && !zigzag) {
+    qr[0].pos0 = rank * (N / W);
+  } else if (rank >= 0) {
+    const int64_t c = N / (2 * W);
+    qr[0] = BwdRun{0, c, rank * c};
+    qr[1] = BwdRun{c, c, (2 * W - 1 - rank) * c};
+  }
+  set_runs(p.q, &p.nq, qr, 2);
+  const BwdRun kr = BwdRun{0, N, 0};
+  set_runs(p.k, &p.nk, &kr, 1);
+  if (Nq == 0 && N == 0) return RATTN_OK;
+  if (Nq > 0) {
+    hipError_t e = launch_bwd_delta(dtype, d, out, dout, delta_ws, (int64_t)B * Nq * Hq,
+                                    (hipStream_t)stream);
+    if (e != hipSuccess) return RATTN_EHIP;
+  }
+  return bwd_dispatch(dtype, d, q, k, v, dout, lse, delta_ws, dq, dk, dv, p, stream);
+}
+
+extern "C" int rattn_bwd_step(const void* q, const void* k, const void* v, const void* dout,
+                              const float* lse, const float* delta, float* dq_acc,
+                              float* dk_acc, float* dv_acc, int B, int Hq, int Hkv,
+                              int64_t q_rows, int64_t q_off, int64_t Nq, int64_t k_rows,
+                              int64_t k_off, int64_t Nk, int d, int dtype, float scale,
+                              int causal, const int64_t* q_seg_start, const int64_t* q_seg_len,
+                              const int64_t* k_seg_start, const int64_t* k_seg_len,
+                              void* stream) {
+  using namespace rattn;
+  if (!q_seg_start || !q_seg_len || !k_seg_start || !k_seg_len) return RATTN_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
+  if (Nq < 0 || Nk < 0 || q_off < 0 || k_off < 0 || q_rows < 0 || k_rows < 0)
+    return RATTN_EINVAL;
+  if (q_off > q_rows || Nq > q_rows - q_off || k_off > k_rows || Nk > k_rows - k_off)
+    return RATTN_EINVAL;
+  if ((Nq > 0 && (!q || !dout || !lse || !delta || !dq_acc)) ||
+      (Nk > 0 && (!k || !v || !dk_acc || !dv_acc)))
+    return RATTN_EINVAL;
+  int rc = check_dtype_d(dtype, d);
+  if (rc != RATTN_OK) return rc;
+  if (causal != 0 && causal != 1) return RATTN_EINVAL;
+  for (int i = 0; i < 2; ++i)
+    if (q_seg_len[i] < 0 || k_seg_len[i] < 0) return RATTN_EINVAL;
+  if (q_seg_len[0] + q_seg_len[1] != Nq || k_seg_len[0] + k_seg_len[1] != Nk)
+    return RATTN_EINVAL;
+  const void* p16[] = {q, k, v, dout, dq_acc, dk_acc, dv_acc};
+  for (const void* x : p16)
+    if (!aligned(x, 16)) return RATTN_EINVAL;
+  if (!aligned(lse, 4) || !aligned(delta, 4)) return RATTN_EINVAL;
+  const int64_t rows_max = std::max(q_rows, k_rows);
+  if (!tensor_ok(B, rows_max, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
+  if (Nq == 0 || Nk == 0) return RATTN_OK;  // no pair: nothing to add
+
+  BwdParams p = make_bwd_params(B, Hq, Hkv, resolve_scale(scale, d));
+  p.causal = causal;
+  p.accumulate = 1;
+  p.q_rows = q_rows;
+  p.q_off = q_off;
+  p.k_rows = k_rows;
+  p.k_off = k_off;
+  const BwdRun qr[2] = {BwdRun{0, q_seg_len[0], q_seg_start[0]},
+                        BwdRun{q_seg_len[0], q_seg_len[1], q_seg_start[1]}};
+  const BwdRun kr[2] = {BwdRun{0, k_seg_len[0], k_seg_start[0]},
+                        BwdRun{k_seg_len[0], k_seg_len[1], k_seg_start[1]}};
+  set_runs(p.q, &p.nq, qr, 2);
+  set_runs(p.k, &p.nk, kr, 2);
+  return bwd_dispatch(dtype, d, q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, p, stream);
 }
 
 extern "C" const char* rattn_status_string(int status) {

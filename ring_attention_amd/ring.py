@@ -104,3 +104,51 @@ def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag
         bo, bl = hook("step", lambda: binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale))
         hook("merge", lambda: binding.merge(out, lse, bo, bl, row_off=row_off))
     return out, lse
+
+
+def ring_backward_steps(q_shard: torch.Tensor, k_shards, v_shards, out_shard: torch.Tensor,
+                        lse_shard: torch.Tensor, dout_shard: torch.Tensor, W: int, zigzag: bool,
+                        rank: int, causal: bool = True, scale: float | None = None,
+                        hook=_direct):
+    """Run device ``rank``'s W backward ring steps (youngju.dev "Ring
+    Attention" analysis, ring_attention_backward; Twinkle page, backward
+    section): D = rowsum(dO * O) once, then at every step the pairs of the
+    forward's step rules, adding to dQ of the local queries and to dK, dV of
+    the held key/value shard, which in a real ring travel back to the shard's
+    owner (here: one float32 accumulator per shard).
+
+    out_shard (q's dtype) and lse_shard are the device's forward results.
+    Returns (dq float32 [B, Nq, Hq, d], dk_acc, dv_acc), the last two lists
+    indexed by source device, each float32 in that device's shard layout.
+    hook(kind, fn) as in ``ring_forward_steps`` ("delta" or "step").
+    """
+    N = sum(k.shape[1] for k in k_shards)
+    delta = hook("delta", lambda: binding.bwd_delta(out_shard, dout_shard))
+    dq = torch.zeros(q_shard.shape, dtype=torch.float32, device=q_shard.device)
+    dk_acc = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in k_shards]
+    dv_acc = [torch.zeros(v.shape, dtype=torch.float32, device=v.device) for v in v_shards]
+    q_runs = shard_rows(N, W, zigzag, rank)
+    Nq_all = q_shard.shape[1]
+    for s in range(W):
+        src = (rank - s) % W
+        k_runs = shard_rows(N, W, zigzag, src)
+        Nk_all = k_shards[src].shape[1]
+        q_off, Nq, k_off, Nk = 0, Nq_all, 0, Nk_all
+        qr, kr, step_causal = q_runs, k_runs, causal
+        if zigzag and causal:
+            c = N // (2 * W)
+            if s == 0:
+                pass
+            elif s <= rank:
+                Nk, kr, step_causal = c, k_runs[:1], False
+            else:
+                q_off, Nq, qr, step_causal = c, c, q_runs[1:], False
+        elif causal:
+            if src > rank:
+                continue
+            step_causal = src == rank
+        hook("step", lambda: binding.bwd_step(
+            q_shard, k_shards[src], v_shards[src], dout_shard, lse_shard, delta, dq,
+            dk_acc[src], dv_acc[src], step_causal, qr, kr, q_off=q_off, Nq=Nq, k_off=k_off,
+            Nk=Nk, scale=scale))
+    return dq, dk_acc, dv_acc

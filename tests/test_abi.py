@@ -188,3 +188,67 @@ def test_binding_checks_tensors_before_calling():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         binding.load_library(str(tmp_path / "librattn.so"))
+
+
+# ---- backward entry points --------------------------------------------------
+
+def bwd(lib, q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4], dout=P[5], dq=P[6], dk=P[7],
+        dv=P[7] + 0x100000, ws=P[7] + 0x200000, B=1, Hq=2, Hkv=2, Nq=64, N=64, d=64, dtype=2,
+        scale=0.0, causal=1, W=1, zigzag=0, rank=-1):
+    return lib.rattn_bwd(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Nq, N, d, dtype,
+                         scale, causal, W, zigzag, rank, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), EINVAL), (dict(dout=0), EINVAL), (dict(dq=0), EINVAL), (dict(dk=0), EINVAL),
+    (dict(ws=0), EINVAL), (dict(lse=0), EINVAL), (dict(B=0), EINVAL),
+    (dict(Hq=3, Hkv=2), EINVAL), (dict(d=48), EUNSUP), (dict(dtype=3), EINVAL),
+    (dict(causal=2), EINVAL), (dict(W=0), EINVAL), (dict(W=33), EUNSUP),
+    (dict(W=3), EINVAL), (dict(W=4, zigzag=1, N=68, Nq=68), EINVAL), (dict(W=4, rank=4), EINVAL),
+    (dict(W=4, rank=1, Nq=64), EINVAL), (dict(dout=P[5] + 8), EINVAL),
+    (dict(dv=P[7] + 0x100008), EINVAL), (dict(ws=P[7] + 0x200002), EINVAL),
+])
+def test_bwd_rejects(rattn_lib, kw, status):
+    assert bwd(rattn_lib, **kw) == status
+
+
+def test_bwd_empty_is_ok_without_launch(rattn_lib):
+    assert bwd(rattn_lib, N=0, Nq=0) == OK
+    assert bwd(rattn_lib, q=0, k=0, v=0, out=0, lse=0, dout=0, dq=0, dk=0, dv=0, ws=0, N=0,
+               Nq=0) == OK
+
+
+def bwd_step(lib, q=P[0], k=P[1], v=P[2], dout=P[3], lse=P[4], delta=P[5], dq=P[6], dk=P[7],
+             dv=P[7] + 0x100000, B=1, Hq=2, Hkv=1, q_rows=64, q_off=0, Nq=64, k_rows=64,
+             k_off=0, Nk=64, d=64, dtype=2, scale=0.0, causal=1, qs=(0, 32), ql=(32, 32),
+             ks=(0, 32), kl=(32, 32)):
+    arr = lambda t: (ctypes.c_int64 * 2)(*t)  # noqa: E731
+    return lib.rattn_bwd_step(q, k, v, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, q_rows, q_off,
+                              Nq, k_rows, k_off, Nk, d, dtype, scale, causal, arr(qs), arr(ql),
+                              arr(ks), arr(kl), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), EINVAL), (dict(delta=0), EINVAL), (dict(dk=0), EINVAL),
+    (dict(Hq=3, Hkv=2), EINVAL),
+    (dict(d=8), EUNSUP), (dict(q_off=8), EINVAL), (dict(k_off=-1), EINVAL),
+    (dict(Nq=65), EINVAL), (dict(ql=(32, 31)), EINVAL), (dict(kl=(-1, 65)), EINVAL),
+    (dict(q_rows=128, q_off=96, Nq=64, ql=(64, 0)), EINVAL),
+    (dict(dq=P[6] + 4), EINVAL), (dict(causal=3), EINVAL),
+])
+def test_bwd_step_rejects(rattn_lib, kw, status):
+    assert bwd_step(rattn_lib, **kw) == status
+
+
+def test_bwd_step_without_pairs_is_ok(rattn_lib):
+    assert bwd_step(rattn_lib, Nk=0, kl=(0, 0)) == OK
+    assert bwd_step(rattn_lib, q_rows=128, q_off=128, Nq=0, ql=(0, 0), qs=(0, 0)) == OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P[0], P[1], P[2], -1, 64, 2), EINVAL), ((0, P[1], P[2], 8, 64, 2), EINVAL),
+    ((P[0], P[1], P[2], 8, 24, 2), EUNSUP), ((P[0], P[1], P[2], 8, 64, 5), EINVAL),
+    ((P[0] + 8, P[1], P[2], 8, 64, 2), EINVAL), ((0, 0, 0, 0, 64, 2), OK),
+])
+def test_bwd_delta_rejects(rattn_lib, args, status):
+    assert rattn_lib.rattn_bwd_delta(*args, None) == status
