@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "librattn.so")
 ARCH = os.environ.get("RATTN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["rattn_abi.hip", "fwd_generic.hip", "fwd_mfma.hip", "fwd_mfma128.hip", "merge.hip",
-           "bwd_generic.hip"]
+           "bwd_generic.hip", "bwd_mfma.hip"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

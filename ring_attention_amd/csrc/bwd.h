@@ -77,4 +77,9 @@ hipError_t launch_bwd_generic(int dtype, int d, const void* q, const void* k, co
                               const void* dout, const float* lse, const float* delta, void* dq,
                               void* dk, void* dv, const BwdParams& p, hipStream_t stream);
 
+// dQ and dK/dV on the matrix cores: 16-bit inputs (dtype 1 or 2), d = 128.
+hipError_t launch_bwd_mfma(int dtype, const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse, const float* delta, void* dq,
+                           void* dk, void* dv, const BwdParams& p, hipStream_t stream);
+
 }  // namespace rattn

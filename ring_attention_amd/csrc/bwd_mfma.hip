@@ -1,0 +1,565 @@
+// bwd_mfma.hip -- 16-bit attention backward at d = 128 on gfx950 matrix cores.
+//
+// What it computes: the recomputation backward of the youngju.dev "Ring
+// Attention" analysis (ring_attention_backward).  From the forward's
+// log-sum-exp and D = rowsum(dO * O):
+//   P = exp2(S scale log2(e) - lse log2(e)),  dP = dO V^T,  dS = P (dP - D)
+//   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K
+// P and dS are rounded to the input type before they enter a matrix product
+// (the forward does the same with P); dP - D is formed in float32.
+//
+// How, on CDNA4 (v_mfma_f32_32x32x16_{bf16,f16}, 4 wavefronts per workgroup):
+//   * dK/dV kernel: a workgroup owns 128 keys, 32 per wave, and streams tiles
+//     of 64 query rows (Q, dO, lse, D) through LDS.  A wave keeps its keys'
+//     K and V rows in registers as the B operand of S = Q K^T and
+//     dP = dO V^T, whose 32x32 accumulators give each lane one key column and
+//     16 query rows; P and dS then go straight from those registers into the
+//     B operand of dV^T += dO^T P and dK^T += Q^T dS, with the A operands
+//     dO^T and Q^T read by transposing LDS reads (ds_read_b64_tr_b16).  The
+//     query rows of every head of the key/value head's GQA group are
+//     streamed in turn, so dK and dV need no reduction across workgroups.
+//   * dQ kernel: a workgroup owns 128 query rows (Q, dO in registers) and
+//     streams tiles of 64 keys (K, V): S^T = K Q^T and dP^T = V dO^T put one
+//     query per lane, so lse and D are one register each; dQ^T += K^T dS^T
+//     with K^T read transposed from the same LDS tile.
+//   * Tiles move global -> LDS by direct-to-LDS DMA (global_load_lds), double
+//     buffered: tile t+1 is requested before the matrix work of tile t and
+//     waited for before the barrier that ends it.  One XOR swizzle serves both
+//     LDS read patterns of a tile: 16-byte chunk c of row r sits at chunk
+//     slot c ^ (4 (r mod 4) + (r div 4) mod 4), so the 16 rows of a row-
+//     fragment read and the 4 rows x 4 chunks of a transposing read land in
+//     distinct banks.
+//   * Causal: the dQ kernel visits the live prefix of key tiles; the dK/dV
+//     kernel starts each query run at the first row that can see its keys.
+//     A wave skips the matrix work of a tile none of its pairs sees; element
+//     masks only on diagonal or ragged tiles.
+#include "bwd.h"
+
+namespace rattn {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int KS = D / 16;                  // k-steps of a contraction over d
+constexpr int DB = D / 32;                  // 32-row blocks of d
+constexpr int kRowBytes = D * 2;
+constexpr int kThreads = 256;               // 4 wavefronts
+constexpr int kRows = 64;                   // rows of a streamed tile
+constexpr int kTileBytes = kRows * kRowBytes;  // 16 KB
+constexpr int kOwn = 128;                   // rows a workgroup owns (32 per wave)
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory");
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// chunk-slot swizzle of row r (see the file comment)
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+__device__ __forceinline__ v4s read_tr(const char* lds, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(
+          (__attribute__((address_space(3))) char*)(lds + off)));
+}
+
+// Per-lane byte offsets of the two LDS read patterns inside one tile.
+//   row[ks]: 8 elements of row l%32, columns 16 ks + 8 (l/32) .. +7 (the A
+//     operand X[32 rows, 16 cols]); add 32 b rows for row block b.
+//   tr[db][s]: transposing read s of the A operand X^T[32 columns of d block
+//     db, 16 rows]: lane l gets column 32 db + l%32 of rows 8 s + 4 (l/32)
+//     .. +3, so the pair (s = 0, 1) covers rows {0..3, 8..11} + 4 (l/32), the
+//     row order of the accumulator registers r = 0..7 (key 8 (r/4) +
+//     4 (l/32) + r%4); add 16 u rows for row group u.
+struct FragOff {
+  uint32_t row[KS];
+  uint32_t tr[DB][2];
+};
+__device__ __forceinline__ FragOff frag_offsets(int lane) {
+  const int hl = lane >> 5, l32 = lane & 31, l16 = lane & 15;
+  FragOff f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    f.row[ks] = (uint32_t)(l32 * kRowBytes + 16 * ((2 * ks + hl) ^ swz(l32)));
+  const int qrow = l16 >> 2;
+  const int c_in = 2 * ((lane >> 4) & 1) + ((l16 & 3) >> 1);
+  const int half = (l16 & 1) * 8;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r = 8 * s + 4 * hl + qrow;
+      f.tr[db][s] = (uint32_t)(r * kRowBytes + 16 * ((4 * db + c_in) ^ swz(r)) + half);
+    }
+  return f;
+}
+
+template <typename TT>
+__device__ __forceinline__ typename TT::v8 row_frag(const char* tile, const FragOff& f, int ks,
+                                                    int row_block) {
+  return *(const typename TT::v8*)(tile + f.row[ks] + row_block * 32 * kRowBytes);
+}
+template <typename TT>
+__device__ __forceinline__ typename TT::v8 tr_frag(const char* tile, const FragOff& f, int db,
+                                                   int row16) {
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const uint32_t o = (uint32_t)(row16 * 16 * kRowBytes);
+  const v4s lo = read_tr(tile, f.tr[db][0] + o);
+  const v4s hi = read_tr(tile, f.tr[db][1] + o);
+  const v8s x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(typename TT::v8, x);
+}
+
+// Request one 64-row tile of a [.., d] tensor: rows row0 .. row0+rows-1 of
+// the flattened row space (stride `stride` elements between rows); rows past
+// `rows` repeat the last one (finite, masked by the caller).  This wave moves
+// rows 16 w .. 16 w + 15, four 1 KB blocks.
+template <typename E>
+__device__ __forceinline__ void dma_tile(const E* base, int64_t row0, int rows, int64_t stride,
+                                         uint32_t lds_tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wave + 4 * i + (lane >> 4);
+    const int rc = r < rows ? r : rows - 1;
+    const char* src = (const char*)(base + (row0 + rc) * stride) +
+                      16 * ((lane & 15) ^ swz(r));
+    dma16(src, lds_tile + (uint32_t)((16 * wave + 4 * i) * kRowBytes));
+  }
+}
+
+__device__ __forceinline__ float lse2_of(float lse) {
+  // rows that saw no key (lse = -inf) get +inf: P = exp2(x - inf) = 0
+  return lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+}
+
+// Pack 16 float32 accumulator values (rows r = 0..15 of one 32-row block)
+// into 8 dwords of input-type pairs, register pair (r, r+1) -> dword r/2.
+template <typename TT>
+__device__ __forceinline__ void pack_pair(float* dst, float a, float b) {
+  using E2 = typename TT::v2;
+  const E2 pr = {to_elem<TT>(a), to_elem<TT>(b)};
+  *dst = __builtin_bit_cast(float, pr);
+}
+template <typename TT>
+__device__ __forceinline__ typename TT::v8 packed_operand(const float* w, int u) {
+  const f32x4 x = {w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
+  return __builtin_bit_cast(typename TT::v8, x);
+}
+
+// ---- dK, dV ------------------------------------------------------------------
+template <typename TT, bool ACC>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
+    const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
+    const typename TT::elem* __restrict__ v, const typename TT::elem* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, void* __restrict__ dk,
+    void* __restrict__ dv, BwdParams p) {
+  using E = typename TT::elem;
+  using v8 = typename TT::v8;
+  constexpr int kStat = 2 * kTileBytes;          // lse, then D, 64 floats each
+  constexpr int kBufBytes = kStat + 2 * kRows * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int32_t BH = p.B * p.Hkv;
+  const int32_t bh = blockIdx.x % BH;
+  const int64_t tl = blockIdx.x / BH;
+  const int32_t b = bh / p.Hkv, hkv = bh % p.Hkv;
+  const BwdTile kt = bwd_tile(p.k, p.nk, kOwn, tl);
+  const int wk0 = 32 * wave;
+  const int wkrows = kt.rows - wk0 < 0 ? 0 : (kt.rows - wk0 > 32 ? 32 : (int)(kt.rows - wk0));
+  const bool k_valid = l32 < wkrows;
+  const int64_t wkpos = kt.pos0 + wk0;      // position of the wave's first key
+  const int64_t kpos = wkpos + l32;         // this lane's key
+  const int64_t krow =
+      ((int64_t)b * p.k_rows + p.k_off + kt.row0 + wk0 + (k_valid ? l32 : 0)) * p.Hkv + hkv;
+
+  // this lane's key as the B operand: 8 dims 16 ks + 8 hl .. +7
+  v8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (k_valid) {
+      kf[ks] = *(const v8*)(k + krow * D + 16 * ks + 8 * hl);
+      vf[ks] = *(const v8*)(v + krow * D + 16 * ks + 8 * hl);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = (typename TT::elem)0.f;
+    }
+  }
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16{};
+
+  // query tiles: every head of the group, each run from the first row that
+  // can see one of this workgroup's keys
+  int64_t st[2] = {0, 0}, nt[2] = {0, 0};
+  for (int ri = 0; ri < p.nq; ++ri) {
+    int64_t s0 = 0;
+    if (p.causal) {
+      s0 = kt.pos0 - p.q[ri].pos0;
+      s0 = s0 < 0 ? 0 : (s0 > p.q[ri].len ? p.q[ri].len : s0);
+    }
+    st[ri] = s0;
+    nt[ri] = (p.q[ri].len - s0 + kRows - 1) / kRows;
+  }
+  const int64_t per_head = nt[0] + nt[1];
+  const int64_t T = per_head * p.group;
+  struct QT {
+    int64_t row0;  // flattened row index in [B * q_rows]
+    int64_t pos0;
+    int32_t hq;
+    int rows;
+  };
+  auto tile_of = [&](int64_t t) {
+    QT x;
+    const int64_t g = t / per_head;
+    int64_t r = t - g * per_head;
+    const int ri = r < nt[0] ? 0 : 1;
+    if (ri) r -= nt[0];
+    const int64_t i0 = st[ri] + r * kRows;
+    const int64_t rem = p.q[ri].len - i0;
+    x.rows = rem < kRows ? (int)rem : kRows;
+    x.row0 = (int64_t)b * p.q_rows + p.q_off + p.q[ri].row0 + i0;
+    x.pos0 = p.q[ri].pos0 + i0;
+    x.hq = hkv * p.group + (int32_t)g;
+    return x;
+  };
+  const int64_t qstride = (int64_t)p.Hq * D;
+  auto issue = [&](int64_t t, int buf) {
+    const QT x = tile_of(t);
+    const uint32_t base = smem_addr + buf * kBufBytes;
+    dma_tile(q + (int64_t)x.hq * D, x.row0, x.rows, qstride, base, wave, lane);
+    dma_tile(dout + (int64_t)x.hq * D, x.row0, x.rows, qstride, base + kTileBytes, wave, lane);
+    if (wave < 2) {
+      const int rc = lane < x.rows ? lane : x.rows - 1;
+      const float* src = (wave == 0 ? lse : delta) + (x.row0 + rc) * p.Hq + x.hq;
+      dma4(src, base + kStat + wave * kRows * 4);
+    }
+  };
+
+  const FragOff fo = frag_offsets(lane);
+  auto compute = [&](int64_t t, int buf) {
+    const QT x = tile_of(t);
+    const char* qb_l = smem + buf * kBufBytes;
+    const char* gb_l = qb_l + kTileBytes;
+    const float* lse_l = (const float*)(qb_l + kStat);
+    const float* dl_l = lse_l + kRows;
+    if (wkrows == 0) return;
+    if (p.causal && x.pos0 + x.rows - 1 < wkpos) return;  // no query of the tile sees a key
+    const bool need_mask = x.rows < kRows || (p.causal && x.pos0 < wkpos + wkrows - 1);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (32 * qb >= x.rows) break;
+      if (p.causal && x.pos0 + 32 * qb + 31 < wkpos) continue;
+      f32x16 s_acc = {}, dp_acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s_acc = TT::mfma32x32x16(row_frag<TT>(qb_l, fo, ks, qb), kf[ks], s_acc);
+        dp_acc = TT::mfma32x32x16(row_frag<TT>(gb_l, fo, ks, qb), vf[ks], dp_acc);
+      }
+      // query row of register r: 32 qb + 8 (r/4) + 4 hl + r%4
+      f32x4 lv[4], dv4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lv[j] = *(const f32x4*)(lse_l + 32 * qb + 8 * j + 4 * hl);
+        dv4[j] = *(const f32x4*)(dl_l + 32 * qb + 8 * j + 4 * hl);
+      }
+      // visible iff the row exists and (causal) the key is not after it:
+      // row index - rel >= 0 with rel = kpos - (x.pos0 + 32 qb + 4 hl)
+      const int64_t rel64 = kpos - (x.pos0 + 32 * qb + 4 * hl);
+      const int rel = rel64 > 64 ? 64 : (rel64 < -64 ? -64 : (int)rel64);
+      const int rlim = x.rows - 32 * qb - 4 * hl;  // rows r2 < rlim exist
+      float pw[8], dw[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float pr[2], ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int rr = r + e;
+          const int r2 = 8 * (rr >> 2) + (rr & 3);
+          const float l2 = lse2_of(lv[rr >> 2][rr & 3]);
+          bool vis = true;
+          if (need_mask) vis = r2 < rlim && (!p.causal || r2 >= rel);
+          const float x2 = exp2_fast(fmaf(s_acc[rr], p.c, -l2));
+          pr[e] = vis ? x2 : 0.f;
+          ds[e] = pr[e] * (dp_acc[rr] - dv4[rr >> 2][rr & 3]);
+        }
+        pack_pair<TT>(&pw[r >> 1], pr[0], pr[1]);
+        pack_pair<TT>(&dw[r >> 1], ds[0], ds[1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v8 pu = packed_operand<TT>(pw, u);
+        const v8 du = packed_operand<TT>(dw, u);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dva[db] = TT::mfma32x32x16(tr_frag<TT>(gb_l, fo, db, 2 * qb + u), pu, dva[db]);
+          dka[db] = TT::mfma32x32x16(tr_frag<TT>(qb_l, fo, db, 2 * qb + u), du, dka[db]);
+        }
+      }
+    }
+  };
+
+  if (T > 0) {
+    issue(0, 0);
+    wait_dma();
+    __syncthreads();
+    for (int64_t t = 0; t < T; ++t) {
+      if (t + 1 < T) issue(t + 1, (int)((t + 1) & 1));
+      compute(t, (int)(t & 1));
+      wait_dma();
+      __syncthreads();
+    }
+  }
+
+  if (!k_valid) return;
+  // lane: key l%32; register 4 j + e of block db: dim 32 db + 8 j + 4 hl + e
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * db + 8 * j + 4 * hl;
+      f32x4 gk, gv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gk[e] = dka[db][4 * j + e] * p.scale;
+        gv[e] = dva[db][4 * j + e];
+      }
+      if (ACC) {
+        f32x4* ok = (f32x4*)((float*)dk + krow * D + d0);
+        f32x4* ov = (f32x4*)((float*)dv + krow * D + d0);
+        *ok = *ok + gk;
+        *ov = *ov + gv;
+      } else {
+        typename TT::v4 ek, ev;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ek[e] = to_elem<TT>(gk[e]);
+          ev[e] = to_elem<TT>(gv[e]);
+        }
+        *(typename TT::v4*)((E*)dk + krow * D + d0) = ek;
+        *(typename TT::v4*)((E*)dv + krow * D + d0) = ev;
+      }
+    }
+}
+
+// ---- dQ ----------------------------------------------------------------------
+template <typename TT, bool ACC>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
+    const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
+    const typename TT::elem* __restrict__ v, const typename TT::elem* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, void* __restrict__ dq,
+    BwdParams p) {
+  using E = typename TT::elem;
+  using v8 = typename TT::v8;
+  constexpr int kBufBytes = 2 * kTileBytes;  // K, V
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int32_t BH = p.B * p.Hq;
+  const int32_t bh = blockIdx.x % BH;
+  const int64_t tl = blockIdx.x / BH;
+  const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
+  const BwdTile qt = bwd_tile(p.q, p.nq, kOwn, tl);
+  const int wq0 = 32 * wave;
+  const int wqrows = qt.rows - wq0 < 0 ? 0 : (qt.rows - wq0 > 32 ? 32 : (int)(qt.rows - wq0));
+  const bool q_valid = l32 < wqrows;
+  const int64_t wqlo = qt.pos0 + wq0;
+  const int64_t wqhi = wqlo + wqrows - 1;
+  const int64_t qpos = wqlo + l32;
+  const int64_t qhi = qt.pos0 + qt.rows - 1;
+  const int64_t qrow =
+      ((int64_t)b * p.q_rows + p.q_off + qt.row0 + wq0 + (q_valid ? l32 : 0)) * p.Hq + hq;
+
+  v8 qf[KS], gf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (q_valid) {
+      qf[ks] = *(const v8*)(q + qrow * D + 16 * ks + 8 * hl);
+      gf[ks] = *(const v8*)(dout + qrow * D + 16 * ks + 8 * hl);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = gf[ks][e] = (typename TT::elem)0.f;
+    }
+  }
+  const float l2 = q_valid ? lse2_of(lse[qrow]) : __builtin_inff();
+  const float dl = q_valid ? delta[qrow] : 0.f;
+  f32x16 dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
+
+  // key tiles: the live prefix of every key run
+  int64_t nt[2] = {0, 0};
+  for (int ri = 0; ri < p.nk; ++ri)
+    nt[ri] = live_tiles(Run{p.k[ri].row0, p.k[ri].len, p.k[ri].pos0}, qhi, p.causal, kRows);
+  const int64_t T = nt[0] + nt[1];
+  struct KT {
+    int64_t row0;
+    int64_t pos0;
+    int rows;
+  };
+  auto tile_of = [&](int64_t t) {
+    KT x;
+    const int ri = t < nt[0] ? 0 : 1;
+    const int64_t tt = ri ? t - nt[0] : t;
+    const int64_t rem = p.k[ri].len - tt * kRows;
+    x.rows = rem < kRows ? (int)rem : kRows;
+    x.row0 = (int64_t)b * p.k_rows + p.k_off + p.k[ri].row0 + tt * kRows;
+    x.pos0 = p.k[ri].pos0 + tt * kRows;
+    return x;
+  };
+  const int64_t kstride = (int64_t)p.Hkv * D;
+  auto issue = [&](int64_t t, int buf) {
+    const KT x = tile_of(t);
+    const uint32_t base = smem_addr + buf * kBufBytes;
+    dma_tile(k + (int64_t)hkv * D, x.row0, x.rows, kstride, base, wave, lane);
+    dma_tile(v + (int64_t)hkv * D, x.row0, x.rows, kstride, base + kTileBytes, wave, lane);
+  };
+
+  const FragOff fo = frag_offsets(lane);
+  auto compute = [&](int64_t t, int buf) {
+    const KT x = tile_of(t);
+    const char* kb_l = smem + buf * kBufBytes;
+    const char* vb_l = kb_l + kTileBytes;
+    if (wqrows == 0) return;
+    if (p.causal && x.pos0 > wqhi) return;  // every key of the tile is after the wave's queries
+    const bool need_mask = x.rows < kRows || (p.causal && x.pos0 + x.rows - 1 > wqlo);
+    f32x16 s_acc[2], dp_acc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s_acc[kb] = f32x16{};
+      dp_acc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s_acc[kb] = TT::mfma32x32x16(row_frag<TT>(kb_l, fo, ks, kb), qf[ks], s_acc[kb]);
+        dp_acc[kb] = TT::mfma32x32x16(row_frag<TT>(vb_l, fo, ks, kb), gf[ks], dp_acc[kb]);
+      }
+    }
+    // key of register r of block kb: 32 kb + 8 (r/4) + 4 hl + r%4; keys
+    // below lim are visible to this lane's query
+    const int lim =
+        (need_mask ? visible_limit(x.rows, p.causal, qpos - x.pos0) : kRows) - 4 * hl;
+    float dw[16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int rr = r + e;
+          const int kk2 = 32 * kb + 8 * (rr >> 2) + (rr & 3);
+          const float x2 = exp2_fast(fmaf(s_acc[kb][rr], p.c, -l2));
+          const float pr = kk2 < lim ? x2 : 0.f;
+          ds[e] = pr * (dp_acc[kb][rr] - dl);
+        }
+        pack_pair<TT>(&dw[8 * kb + (r >> 1)], ds[0], ds[1]);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const v8 du = packed_operand<TT>(dw, u);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqa[db] = TT::mfma32x32x16(tr_frag<TT>(kb_l, fo, db, u), du, dqa[db]);
+    }
+  };
+
+  if (T > 0) {
+    issue(0, 0);
+    wait_dma();
+    __syncthreads();
+    for (int64_t t = 0; t < T; ++t) {
+      if (t + 1 < T) issue(t + 1, (int)((t + 1) & 1));
+      compute(t, (int)(t & 1));
+      wait_dma();
+      __syncthreads();
+    }
+  }
+
+  if (!q_valid) return;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = 32 * db + 8 * j + 4 * hl;
+      f32x4 g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[e] = dqa[db][4 * j + e] * p.scale;
+      if (ACC) {
+        f32x4* o = (f32x4*)((float*)dq + qrow * D + d0);
+        *o = *o + g;
+      } else {
+        typename TT::v4 eg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) eg[e] = to_elem<TT>(g[e]);
+        *(typename TT::v4*)((E*)dq + qrow * D + d0) = eg;
+      }
+    }
+}
+
+template <typename TT, bool ACC>
+hipError_t launch_acc(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                      const BwdParams& p, hipStream_t stream) {
+  using E = typename TT::elem;
+  const int64_t qb = bwd_tiles(p.q, p.nq, kOwn) * p.B * p.Hq;
+  if (qb > 0) {
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<TT, ACC>), dim3((unsigned)qb), dim3(kThreads), 0,
+                       stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,
+                       dq, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t kb = bwd_tiles(p.k, p.nk, kOwn) * p.B * p.Hkv;
+  if (kb > 0) {
+    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<TT, ACC>), dim3((unsigned)kb), dim3(kThreads), 0,
+                       stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,
+                       dk, dv, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <typename TT>
+hipError_t launch_t(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                    const BwdParams& p, hipStream_t stream) {
+  return p.accumulate ? launch_acc<TT, true>(q, k, v, dout, lse, delta, dq, dk, dv, p, stream)
+                      : launch_acc<TT, false>(q, k, v, dout, lse, delta, dq, dk, dv, p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_mfma(int dtype, const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse, const float* delta, void* dq,
+                           void* dk, void* dv, const BwdParams& p, hipStream_t stream) {
+  switch (dtype) {
+    case 1: return launch_t<F16>(q, k, v, dout, lse, delta, dq, dk, dv, p, stream);
+    case 2: return launch_t<Bf16>(q, k, v, dout, lse, delta, dq, dk, dv, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rattn

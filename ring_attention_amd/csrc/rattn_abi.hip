@@ -360,8 +360,11 @@ int bwd_dispatch(int dtype, int d, const void* q, const void* k, const void* v,
   const int64_t g1 = bwd_tiles(p.q, p.nq, 64) * p.B * p.Hq;
   const int64_t g2 = bwd_tiles(p.k, p.nk, 64) * p.B * p.Hkv;
   if (g1 > INT32_MAX || g2 > INT32_MAX) return RATTN_EUNSUPPORTED;
-  hipError_t e = launch_bwd_generic(dtype, d, q, k, v, dout, lse, delta, dq, dk, dv, p,
-                                    (hipStream_t)stream);
+  hipError_t e =
+      (dtype != RATTN_F32 && d == 128)
+          ? launch_bwd_mfma(dtype, q, k, v, dout, lse, delta, dq, dk, dv, p, (hipStream_t)stream)
+          : launch_bwd_generic(dtype, d, q, k, v, dout, lse, delta, dq, dk, dv, p,
+                               (hipStream_t)stream);
   return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
 }
 
