@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--small-d-only", action="store_true",
                     help="run only the small head-dim sweep (after --copy-probe, if given) "
                          "and print its JSON")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="run only the backward measurements and print their JSON")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -308,6 +310,10 @@ def main():
         print(json.dumps({"extras": small_d_sweep(torch, binding, workloads, dev, args)}),
               flush=True)
         return
+    if args.bwd_only:
+        print(json.dumps({"extras": backward_extras(torch, binding, ring, workloads, dev, args)}),
+              flush=True)
+        return
     w = workloads.workload(4)
     W, rank, N, d, Hq = w.W, w.rank, w.N, w.d, w.Hq
     c = N // (2 * W)
@@ -465,12 +471,74 @@ def main():
             del qe, ke, ve
             torch.cuda.empty_cache()
         extras.update(small_d_sweep(torch, binding, workloads, dev, args))
+        extras.update(backward_extras(torch, binding, ring, workloads, dev, args))
         result["extras"] = extras
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
 
     print(json.dumps(result), flush=True)
+
+
+def backward_extras(torch, binding, ring, workloads, dev, args):
+    """Backward (dQ, dK, dV) throughput of the batched causal workload and of
+    the ZigZag ring share: whole-schedule calls (rattn_bwd) and, for the ring
+    share, the device's W backward ring steps (rattn_bwd_delta + rattn_bwd_step).
+    Algorithmic work: 10 d FLOP per visible pair per query head (dP = dO V^T,
+    dV, dK, dQ and the recomputed S: five products of 2 d each); the kernels
+    issue 14 d (the dQ kernel recomputes S and dP)."""
+    res = {}
+    for idx in (3, 4):
+        w = workloads.workload(idx)
+        q, k, v = workloads.make_inputs(w, device=dev)
+        g = torch.Generator(device=dev).manual_seed(1000 + idx)
+        do = workloads.randn(q.shape, q.dtype, g, dev)
+        qpos = runs_positions(ring.shard_rows(w.N, w.W, w.zigzag, w.rank)) \
+            if w.rank >= 0 else np.arange(w.N)
+        pairs = causal_pairs(qpos, np.arange(w.N)) if w.causal else w.Nq * w.N
+        flop = 10 * w.d * w.Hq * w.B * pairs
+        out, lse = binding.fwd(q, k, v, causal=w.causal, n_ring_steps=w.W, zigzag=w.zigzag,
+                               rank=w.rank)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+
+        def run():
+            return binding.bwd(q, k, v, out, lse, do, causal=w.causal, n_ring_steps=w.W,
+                               zigzag=w.zigzag, rank=w.rank, dq=dq, dk=dk, dv=dv, delta_ws=ws)
+        reps = max(3, args.steps // 2)
+        for _ in range(max(1, args.warmup)):
+            run()
+        te = Timer(torch)
+        for _ in range(reps):
+            te(run)
+        ms = te.total_ms() / reps
+        tf = flop / (ms * 1e-3) / 1e12
+        res[w.name + "_bwd"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                                "flop": flop, "flop_rule": "10 d per visible pair per head"}
+        if idx == 4:
+            ks = [ring.shard(k, w.W, True, r) for r in range(w.W)]
+            vs = [ring.shard(v, w.W, True, r) for r in range(w.W)]
+
+            def run_steps():
+                return ring.ring_backward_steps(q, ks, vs, out, lse, do, w.W, True, w.rank,
+                                                causal=True)
+            for _ in range(max(1, args.warmup)):
+                run_steps()
+            te = Timer(torch)
+            for _ in range(reps):
+                te(run_steps)
+            ms = te.total_ms() / reps
+            tf = flop / (ms * 1e-3) / 1e12
+            res[w.name + "_bwd_ring_steps"] = {
+                "ms": round(ms, 4), "tflops": round(tf, 2),
+                "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                "mode": "rattn_bwd_delta + 8 rattn_bwd_step launches into float32 "
+                        "accumulators (zeroing included)"}
+            del ks, vs
+        del q, k, v, do, out, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def small_d_sweep(torch, binding, workloads, dev, args):

@@ -157,6 +157,27 @@ __device__ __forceinline__ typename TT::v8 packed_operand(const float* w, int u)
   return __builtin_bit_cast(typename TT::v8, x);
 }
 
+// Work order.  The dispatcher deals workgroups to the 8 XCDs round-robin
+// (workgroup id % 8), and each XCD has its own L2.  Give every XCD whole
+// (batch, head) pairs, their tiles consecutive in its sequence, so that the
+// workgroups an XCD runs at the same time stream the same head's tiles
+// (K/V, or Q/dO) through its L2.  heavy_last: a head's tiles are taken
+// from the last one (causal dQ: later query tiles see more keys).
+__device__ __forceinline__ void work_order(int32_t BH, int64_t n_tiles, bool heavy_last,
+                                           int32_t* bh, int64_t* tl) {
+  const uint32_t id = blockIdx.x;
+  if ((BH & 7) == 0) {
+    const uint32_t x = id & 7, j = id >> 3;
+    const int64_t t = (int64_t)j % n_tiles;
+    *bh = (int32_t)(x + 8 * (uint32_t)((int64_t)j / n_tiles));
+    *tl = heavy_last ? n_tiles - 1 - t : t;
+  } else {
+    *bh = (int32_t)(id % (uint32_t)BH);
+    const int64_t t = id / (uint32_t)BH;
+    *tl = heavy_last ? n_tiles - 1 - t : t;
+  }
+}
+
 // ---- dK, dV ------------------------------------------------------------------
 template <typename TT, bool ACC>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
@@ -178,8 +199,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
   const int l32 = lane & 31;
 
   const int32_t BH = p.B * p.Hkv;
-  const int32_t bh = blockIdx.x % BH;
-  const int64_t tl = blockIdx.x / BH;
+  int32_t bh;
+  int64_t tl;
+  work_order(BH, bwd_tiles(p.k, p.nk, kOwn), false, &bh, &tl);
   const int32_t b = bh / p.Hkv, hkv = bh % p.Hkv;
   const BwdTile kt = bwd_tile(p.k, p.nk, kOwn, tl);
   const int wk0 = 32 * wave;
@@ -379,8 +401,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
   const int l32 = lane & 31;
 
   const int32_t BH = p.B * p.Hq;
-  const int32_t bh = blockIdx.x % BH;
-  const int64_t tl = blockIdx.x / BH;
+  int32_t bh;
+  int64_t tl;
+  work_order(BH, bwd_tiles(p.q, p.nq, kOwn), p.causal != 0, &bh, &tl);
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
   const BwdTile qt = bwd_tile(p.q, p.nq, kOwn, tl);
   const int wq0 = 32 * wave;
