@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--small-d-only", action="store_true",
                     help="run only the small head-dim sweep (after --copy-probe, if given) "
                          "and print its JSON")
+    ap.add_argument("--layouts-only", action="store_true",
+                    help="run only the causal layout comparison and print its JSON")
     ap.add_argument("--bwd-only", action="store_true",
                     help="run only the backward measurements and print their JSON")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
@@ -310,6 +312,10 @@ def main():
         print(json.dumps({"extras": small_d_sweep(torch, binding, workloads, dev, args)}),
               flush=True)
         return
+    if args.layouts_only:
+        print(json.dumps({"extras": layout_comparison(torch, binding, ring, workloads, dev,
+                                                      args)}), flush=True)
+        return
     if args.bwd_only:
         print(json.dumps({"extras": backward_extras(torch, binding, ring, workloads, dev, args)}),
               flush=True)
@@ -472,6 +478,7 @@ def main():
             torch.cuda.empty_cache()
         extras.update(small_d_sweep(torch, binding, workloads, dev, args))
         extras.update(backward_extras(torch, binding, ring, workloads, dev, args))
+        extras.update(layout_comparison(torch, binding, ring, workloads, dev, args))
         result["extras"] = extras
 
     if not args.no_cpu:
@@ -537,6 +544,80 @@ def backward_extras(torch, binding, ring, workloads, dev, args):
                         "accumulators (zeroing included)"}
             del ks, vs
         del q, k, v, do, out, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def tile_efficiency(steps, br=256, bc=64):
+    """Visible pairs / pairs of the tiles a step kernel computes, for a list
+    of (query positions, key positions) steps, each side ascending within
+    its runs; a key tile is computed for a query tile iff its first key is
+    not after the tile's last query."""
+    vis = done = 0
+    for qp, kp in steps:
+        vis += causal_pairs(qp, kp)
+        kfirst = np.asarray(kp)[::bc]
+        krows = np.minimum(bc, len(kp) - np.arange(0, len(kp), bc))
+        for i0 in range(0, len(qp), br):
+            qt = np.asarray(qp[i0:i0 + br])
+            done += len(qt) * int(krows[kfirst <= qt.max()].sum())
+    return vis / done if done else 1.0
+
+
+def layout_comparison(torch, binding, ring, workloads, dev, args):
+    """Causal load balance of the ring layouts at the ZigZag ring share's
+    shape (131072 tokens, 8 devices, 8 heads, d = 128, bf16): every device's
+    W forward ring steps (merges in the step epilogue) timed on this GPU;
+    the ring's step time is the slowest device's, and device_tflops is one
+    device's share of the whole causal attention (4 d per visible pair) over
+    that time.  Contiguous blocks, ZigZag chunk pairs (Twinkle page) and the
+    Striped layout (ultralytics page)."""
+    w = workloads.workload(4)
+    W, N, d, H = w.W, w.N, w.d, w.Hq
+    q, k, v = workloads.make_inputs(workloads.Workload(
+        0, "layouts", 1, N, N, H, w.Hkv, d, w.dtype, True, W, False, -1, 0), device=dev)
+    total_flop = 4 * d * H * (N * (N + 1) // 2)
+    res = {}
+    for layout in ("contiguous", "zigzag", "striped"):
+        if layout == "striped":
+            ks = [ring.stripe(k, W, r) for r in range(W)]
+            vs = [ring.stripe(v, W, r) for r in range(W)]
+            qs = [ring.stripe(q, W, r) for r in range(W)]
+
+            def run(r):
+                return ring.striped_forward_steps(qs[r], ks, vs, W, r)
+            S = N // W
+            steps = [(np.arange(S), np.arange(S) + ring.striped_key_offset(r, (r - s) % W))
+                     for r in range(W) for s in range(W)]
+        else:
+            zz = layout == "zigzag"
+            ks = [ring.shard(k, W, zz, r) for r in range(W)]
+            vs = [ring.shard(v, W, zz, r) for r in range(W)]
+            qs = [ring.shard(q, W, zz, r) for r in range(W)]
+
+            def run(r, zz=zz):
+                return ring.ring_forward_steps(qs[r], ks, vs, W, zz, r, causal=True)
+            steps = []
+            for r in range(W):
+                qp = runs_positions(ring.shard_rows(N, W, zz, r))
+                for s in range(W):
+                    src = (r - s) % W
+                    steps.append((qp, runs_positions(ring.shard_rows(N, W, zz, src))))
+        for r in range(W):  # warm every device's share first
+            run(r)
+        ms = []
+        for r in range(W):
+            te = Timer(torch)
+            for _ in range(3):
+                te(lambda: run(r))
+            ms.append(te.total_ms() / 3)
+        ring_ms = max(ms)
+        res["layout_" + layout] = {
+            "device_ms": [round(x, 3) for x in ms], "ring_step_ms": round(ring_ms, 3),
+            "imbalance_max_over_mean": round(ring_ms / (sum(ms) / W), 3),
+            "device_tflops": round(total_flop / W / (ring_ms * 1e-3) / 1e12, 1),
+            "tile_efficiency": round(tile_efficiency(steps), 4)}
+        del ks, vs, qs
         torch.cuda.empty_cache()
     return res
 

@@ -68,3 +68,21 @@ def zigzag_step_plan(W: int, rank: int, step: int, c: int):
     if step <= rank:
         return all_rows, front, False, src
     return back, all_rows, False, src
+
+
+def striped_shard_positions(N: int, W: int, rank: int) -> np.ndarray:
+    """Striped layout (ultralytics.com glossary "Ring Attention": Striped
+    Attention gives each device tokens spread evenly over the sequence):
+    device ``rank`` keeps positions rank, rank + W, rank + 2W, ...  (a
+    reading: the page gives the idea, not the map; stride W is the even
+    spread)."""
+    if N % W:
+        raise ValueError("N must be a multiple of W")
+    return np.arange(rank, N, W, dtype=np.int64)
+
+
+def striped_key_offset(rank: int, src: int) -> int:
+    """Striped causal step rule: local query i of device ``rank`` (position
+    rank + W i) sees local key j of device ``src`` (position src + W j) iff
+    j + offset <= i, with offset 0 when src <= rank and 1 when src > rank."""
+    return 0 if src <= rank else 1

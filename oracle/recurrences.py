@@ -242,3 +242,29 @@ def ring_backward(q, k, v, o, lse, do, W: int, rank: int, scale: float | None = 
         dQ += dS @ Kb
         dK[rows] += dS.T @ q
     return dQ, dK, dV
+
+
+def striped_ring_forward(q_shards, k_shards, v_shards, W: int, rank: int,
+                         scale: float | None = None):
+    """One device of a causal ring over the Striped layout: at step s device
+    ``rank`` holds the shard of device (rank - s) mod W (the ultralytics ring
+    order) and attends to it under the striped step rule (layouts.
+    striped_key_offset) in local indices; steps are folded with
+    ``sigmoid_merge``.  Returns (out [S, d], lse [S])."""
+    from .layouts import striped_key_offset
+
+    q = np.asarray(q_shards[rank], np.float64)
+    S, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((S, np.asarray(v_shards[0]).shape[1]))
+    lse = np.full(S, -np.inf)
+    local = np.arange(S)
+    for step in range(W):
+        src = (rank - step) % W
+        k = np.asarray(k_shards[src], np.float64)
+        v = np.asarray(v_shards[src], np.float64)
+        bo, bl = _attend(q, k, v, scale, True, local,
+                         np.arange(k.shape[0]) + striped_key_offset(rank, src))
+        out, lse = sigmoid_merge(out, lse, bo, bl)
+    return out, lse

@@ -152,3 +152,70 @@ def ring_backward_steps(q_shard: torch.Tensor, k_shards, v_shards, out_shard: to
             dk_acc[src], dv_acc[src], step_causal, qr, kr, q_off=q_off, Nq=Nq, k_off=k_off,
             Nk=Nk, scale=scale))
     return dq, dk_acc, dv_acc
+
+
+# ---- Striped layout ---------------------------------------------------------
+# ultralytics.com "Ring Attention": Striped Attention spreads each device's
+# tokens evenly over the sequence, so under the causal mask every device and
+# every ring step gets about the same work.  Device r keeps positions
+# r, r + W, r + 2W, ... (stride W).  Local query i of device r (position
+# r + W i) sees local key j of device src (position src + W j) iff
+# j + off <= i, off = 0 when src <= r, else 1.  Each step is therefore one
+# causal block in local indices, which the step calls express with
+# positions: queries at 0 .. S-1, keys at off .. off + S - 1.
+
+
+def stripe(x: torch.Tensor, W: int, rank: int) -> torch.Tensor:
+    """Rows rank, rank + W, ... of a natural-order [B, N, H, d] tensor, stored
+    contiguously (the shard device ``rank`` holds under the Striped layout)."""
+    return x[:, rank::W].contiguous()
+
+
+def striped_key_offset(rank: int, src: int) -> int:
+    return 0 if src <= rank else 1
+
+
+def striped_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, rank: int,
+                          causal: bool = True, scale: float | None = None, hook=_direct,
+                          fused_merge: bool = True):
+    """Device ``rank``'s W ring steps over the Striped layout; returns float32
+    (out, lse).  q_shard, k_shards[src], v_shards[src] as ``stripe`` gives
+    them; hook and fused_merge as in ``ring_forward_steps``."""
+    S = q_shard.shape[1]
+    out = lse = None
+    for s in range(W):
+        src = (rank - s) % W
+        kb, vb = k_shards[src], v_shards[src]
+        qr = [(0, S)]
+        kr = [(striped_key_offset(rank, src) if causal else 0, kb.shape[1])]
+        if out is None:
+            out, lse = hook("step", lambda: binding.fwd_step(q_shard, kb, vb, causal, qr, kr,
+                                                             scale))
+        elif fused_merge:
+            hook("step", lambda: binding.fwd_step_merge(q_shard, kb, vb, causal, qr, kr, out,
+                                                        lse, scale=scale))
+        else:
+            bo, bl = hook("step", lambda: binding.fwd_step(q_shard, kb, vb, causal, qr, kr,
+                                                           scale))
+            hook("merge", lambda: binding.merge(out, lse, bo, bl))
+    return out, lse
+
+
+def striped_backward_steps(q_shard: torch.Tensor, k_shards, v_shards, out_shard: torch.Tensor,
+                           lse_shard: torch.Tensor, dout_shard: torch.Tensor, W: int, rank: int,
+                           causal: bool = True, scale: float | None = None, hook=_direct):
+    """Backward of ``striped_forward_steps`` (as ``ring_backward_steps``):
+    returns (dq float32, dk_acc, dv_acc) with one float32 accumulator per
+    source device's shard."""
+    S = q_shard.shape[1]
+    delta = hook("delta", lambda: binding.bwd_delta(out_shard, dout_shard))
+    dq = torch.zeros(q_shard.shape, dtype=torch.float32, device=q_shard.device)
+    dk_acc = [torch.zeros(k.shape, dtype=torch.float32, device=k.device) for k in k_shards]
+    dv_acc = [torch.zeros(v.shape, dtype=torch.float32, device=v.device) for v in v_shards]
+    for s in range(W):
+        src = (rank - s) % W
+        kr = [(striped_key_offset(rank, src) if causal else 0, k_shards[src].shape[1])]
+        hook("step", lambda: binding.bwd_step(
+            q_shard, k_shards[src], v_shards[src], dout_shard, lse_shard, delta, dq,
+            dk_acc[src], dv_acc[src], causal, [(0, S)], kr, scale=scale))
+    return dq, dk_acc, dv_acc

@@ -344,6 +344,44 @@ def test_zigzag_ring_equals_causal_attention(W):
         assert np.allclose(so[0, :, 0], o, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("N,W", [(32, 4), (24, 3), (64, 8)])
+def test_striped_layout_spreads_tokens_evenly(N, W):
+    """Every position belongs to exactly one device, and each device's
+    positions are spaced W apart (the ultralytics page's even spread)."""
+    allpos = np.concatenate([layouts.striped_shard_positions(N, W, r) for r in range(W)])
+    assert np.array_equal(np.sort(allpos), np.arange(N))
+    for r in range(W):
+        p = layouts.striped_shard_positions(N, W, r)
+        assert p[0] == r and np.all(np.diff(p) == W)
+
+
+def test_striped_step_rule_is_the_causal_rule():
+    """Brute force: the local rule j + offset <= i is the position rule
+    src + W j <= rank + W i, for every pair of devices and rows."""
+    for W in (1, 2, 3, 5, 8):
+        for rank in range(W):
+            for src in range(W):
+                off = layouts.striped_key_offset(rank, src)
+                for i in range(6):
+                    for j in range(6):
+                        assert (j + off <= i) == (src + W * j <= rank + W * i)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
+def test_striped_ring_equals_causal_attention(W):
+    S, d = 6, 8
+    N = W * S
+    q, k, v = rnd((N, d), 190 + W), rnd((N, d), 200 + W), rnd((N, d), 210 + W)
+    shards = [layouts.striped_shard_positions(N, W, r) for r in range(W)]
+    full_o, full_l = oracle.attention(q[None, :, None], k[None, :, None], v[None, :, None],
+                                      causal=True)
+    for r in range(W):
+        o, l = recurrences.striped_ring_forward([q[s] for s in shards], [k[s] for s in shards],
+                                                [v[s] for s in shards], W, r)
+        assert np.allclose(o, full_o[0, shards[r], 0], rtol=0, atol=1e-12)
+        assert np.allclose(l, full_l[0, shards[r], 0], rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("W,rank", [(4, 0), (4, 3), (3, 1)])
 def test_contiguous_ring_causal_equals_blocks(W, rank):
     """Contiguous ring: causal attention of device r's block over all key blocks
