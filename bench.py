@@ -479,6 +479,7 @@ def main():
         extras.update(small_d_sweep(torch, binding, workloads, dev, args))
         extras.update(backward_extras(torch, binding, ring, workloads, dev, args))
         extras.update(layout_comparison(torch, binding, ring, workloads, dev, args))
+        extras.update(varlen_extra(torch, binding, workloads, dev, args))
         result["extras"] = extras
 
     if not args.no_cpu:
@@ -620,6 +621,34 @@ def layout_comparison(torch, binding, ring, workloads, dev, args):
         del ks, vs, qs
         torch.cuda.empty_cache()
     return res
+
+
+def varlen_extra(torch, binding, workloads, dev, args):
+    """A packed variable-length batch (rattn_fwd_varlen): 16 causal sequences
+    with lengths drawn uniformly from [1024, 16384] (numpy seed 7), 32 query
+    heads over 8 key/value heads, d = 128, bf16."""
+    lens = [int(x) for x in np.random.default_rng(7).integers(1024, 16385, 16)]
+    N = sum(lens)
+    q, k, v = workloads.make_qkv(1, N, N, 32, 8, 128, torch.bfloat16, seed=7, device=dev)
+    q, k, v = q[0], k[0], v[0]
+    starts, ls = binding.varlen_from_cu_seqlens(np.concatenate([[0], np.cumsum(lens)]))
+    flop = 4 * 128 * 32 * sum(n * (n + 1) // 2 for n in lens)
+
+    def run():
+        return binding.fwd_varlen(q, k, v, starts, ls, starts, ls, causal=True)
+    for _ in range(max(1, args.warmup)):
+        run()
+    te = Timer(torch)
+    reps = max(3, args.steps // 2)
+    for _ in range(reps):
+        te(run)
+    ms = te.total_ms() / reps
+    tf = flop / (ms * 1e-3) / 1e12
+    del q, k, v
+    torch.cuda.empty_cache()
+    return {"varlen_16seq_1k_16k_causal_h32kv8_d128_bf16": {
+        "ms": round(ms, 4), "tflops": round(tf, 2),
+        "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "tokens": N}}
 
 
 def small_d_sweep(torch, binding, workloads, dev, args):

@@ -131,6 +131,30 @@ RATTN_API int rattn_merge(float* out, float* lse, const float* blk_out, const fl
                 void* stream);
 
 /*
+ * Variable-length (packed or padded) batch: n_seq independent sequences in
+ * one launch (the varlen attention of the yz520gzy flash-attn example and of
+ * Twinkle's packed batches).  Sequence i owns query rows
+ * [q_start[i], q_start[i] + q_len[i]) of q [Nq, Hq, d] and key/value rows
+ * [k_start[i], k_start[i] + k_len[i]) of k, v [Nk, Hkv, d]; it attends only
+ * to its own keys.  Packed batches pass prefix sums (start = cu[i],
+ * len = cu[i+1] - cu[i]); padded ones pass each row block's start and the
+ * true length, so pad rows are neither read as keys nor written.
+ * Causal: key j of a sequence sits at position j and query i at
+ * k_len - q_len + i (the last query aligned with the last key; the usual
+ * rule when q_len == k_len).  q_start, q_len, k_start, k_len are DEVICE
+ * arrays of n_seq int32; max_len_q >= every q_len (rows past it are not
+ * computed).  Ranges are clamped to [0, Nq) and [0, Nk) in the kernels, so a
+ * bad range yields wrong rows, never an access outside the tensors.  out
+ * (q's dtype, [Nq, Hq, d]) and lse ([Nq, Hq]) are written only on rows that
+ * belong to a sequence.  Other arguments and errors as rattn_fwd.
+ */
+RATTN_API int rattn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
+                               float* lse, const int32_t* q_start, const int32_t* q_len,
+                               const int32_t* k_start, const int32_t* k_len, int n_seq,
+                               int64_t max_len_q, int64_t Nq, int64_t Nk, int Hq, int Hkv, int d,
+                               int dtype, float scale, int causal, void* stream);
+
+/*
  * rattn_fwd with split-KV: the same schedule and result, with the live
  * key/value tiles of every query tile divided into n_splits contiguous
  * ranges, each processed by its own workgroup, and the n_splits partial

@@ -21,8 +21,8 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # Exported symbols, in the order include/rattn.h declares them.
 EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_fwd_step_merge", "rattn_merge",
-           "rattn_fwd_split", "rattn_split_hint", "rattn_bwd_delta", "rattn_bwd",
-           "rattn_bwd_step", "rattn_status_string")
+           "rattn_fwd_varlen", "rattn_fwd_split", "rattn_split_hint", "rattn_bwd_delta",
+           "rattn_bwd", "rattn_bwd_step", "rattn_status_string")
 
 
 class RattnError(RuntimeError):
@@ -58,6 +58,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                          f32, i32, i64p, i64p, i64p, i64p, i64, i64, vp]
     lib.rattn_merge.restype = i32
     lib.rattn_merge.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp]
+    lib.rattn_fwd_varlen.restype = i32
+    lib.rattn_fwd_varlen.argtypes = [vp] * 9 + [i32, i64, i64, i64, i32, i32, i32, i32, f32,
+                                                i32, vp]
     lib.rattn_fwd_split.restype = i32
     lib.rattn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
                                     i32, i32, i32, i32, i32, vp, i64, vp]
@@ -357,4 +360,56 @@ def bwd_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
         _scale(scale), int(bool(causal)), qs, ql, kst, kl, _stream(q))
     _check("rattn_bwd_step", rc)
     return dq_acc, dk_acc, dv_acc
+
+
+def varlen_from_cu_seqlens(cu_seqlens):
+    """(starts, lengths) of a packed batch given its prefix sums cu_seqlens
+    (n_seq + 1 non-decreasing integers starting at 0)."""
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    if not cu or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0 and not decrease")
+    return cu[:-1], [b - a for a, b in zip(cu, cu[1:])]
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_start, q_len, k_start,
+               k_len, causal: bool = False, scale: float | None = None,
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Variable-length batch (rattn_fwd_varlen): sequence i attends from query
+    rows [q_start[i], +q_len[i]) of q [Nq, Hq, d] to key/value rows
+    [k_start[i], +k_len[i]) of k, v [Nk, Hkv, d].  The ranges are host lists
+    (checked here) copied to the device as int32.  Returns (out [Nq, Hq, d],
+    lse [Nq, Hq]); rows outside every sequence keep what out/lse held
+    (zeros / -inf when allocated here)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3 or not t.is_cuda or \
+                not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D GPU tensor [N, H, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODES or \
+            k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("q, k, v must share dtype and head dim; k, v one shape")
+    Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[0], k.shape[1]
+    ranges = [list(map(int, x)) for x in (q_start, q_len, k_start, k_len)]
+    n_seq = len(ranges[0])
+    if any(len(x) != n_seq for x in ranges):
+        raise ValueError("q_start, q_len, k_start, k_len must have one entry per sequence")
+    for (qs, ql, ks, kl) in zip(*ranges):
+        if qs < 0 or ql < 0 or qs + ql > Nq or ks < 0 or kl < 0 or ks + kl > Nk:
+            raise ValueError("a sequence range lies outside q or k")
+    if out is None:
+        out = torch.zeros_like(q)
+    if lse is None:
+        lse = torch.full((Nq, Hq), float("-inf"), dtype=torch.float32, device=q.device)
+    _like("out", out, q)
+    _like("lse", lse, q, torch.float32)
+    if out.shape != q.shape or lse.shape != (Nq, Hq):
+        raise ValueError("out must be [Nq, Hq, d] and lse [Nq, Hq]")
+    dev = [torch.tensor(x if x else [0], dtype=torch.int32, device=q.device) for x in ranges]
+    max_len_q = max(ranges[1]) if n_seq else 0
+    rc = load_library().rattn_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        *[t.data_ptr() for t in dev], n_seq, max_len_q, Nq, Nk, Hq, Hkv, d,
+        DTYPE_CODES[q.dtype], _scale(scale), int(bool(causal)), _stream(q))
+    _check("rattn_fwd_varlen", rc)
+    return out, lse
 

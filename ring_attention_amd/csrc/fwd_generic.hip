@@ -35,6 +35,7 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(
   const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
   const QTile qt = query_tile(s, t_lin);
+  if (qt.rows <= 0) return;  // varlen: a tile past the end of its sequence
 
   const bool q_valid = lane < qt.rows;
   const int64_t q_pos = qt.pos0 + lane;

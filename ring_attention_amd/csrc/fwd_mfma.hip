@@ -85,6 +85,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
   const QTile qt = query_tile(s, t_lin);
+  if (qt.rows <= 0) return;  // varlen: a tile past the end of its sequence
   const int64_t qhi = qt.pos0 + qt.rows - 1;
 
   const int wq0 = 32 * wave;                 // first row of this wave in the tile

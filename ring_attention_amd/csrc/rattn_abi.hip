@@ -182,6 +182,48 @@ extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out,
   return dispatch(dtype, d, q, k, v, out, lse, false, p, s, (int64_t)s.n_tiles * B * Hq, stream);
 }
 
+extern "C" int rattn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
+                                float* lse, const int32_t* q_start, const int32_t* q_len,
+                                const int32_t* k_start, const int32_t* k_len, int n_seq,
+                                int64_t max_len_q, int64_t Nq, int64_t Nk, int Hq, int Hkv,
+                                int d, int dtype, float scale, int causal, void* stream) {
+  using namespace rattn;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
+  if (n_seq < 0 || max_len_q < 0 || Nq < 0 || Nk < 0) return RATTN_EINVAL;
+  int rc = check_dtype_d(dtype, d);
+  if (rc != RATTN_OK) return rc;
+  if (causal != 0 && causal != 1) return RATTN_EINVAL;
+  if (n_seq == 0 || max_len_q == 0 || Nq == 0) return RATTN_OK;
+  if (!q || !out || !lse || !q_start || !q_len || !k_start || !k_len || (Nk > 0 && (!k || !v)))
+    return RATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(lse, 4) || !aligned(q_start, 4) || !aligned(q_len, 4) || !aligned(k_start, 4) ||
+      !aligned(k_len, 4))
+    return RATTN_EINVAL;
+  if (!tensor_ok(1, std::max(Nq, Nk), Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
+  const int br = tile_rows(dtype, d);
+  const int64_t tiles = (max_len_q + br - 1) / br;
+  if (tiles > INT32_MAX || tiles * n_seq > INT32_MAX) return RATTN_EUNSUPPORTED;
+  Sched s;
+  memset(&s, 0, sizeof s);
+  s.mode = kVisitVarlen;
+  s.W = 1;
+  s.causal = causal;
+  s.reverse = causal ? 1 : 0;
+  s.br = br;
+  s.n_tiles = (int32_t)(tiles * n_seq);
+  s.vl_q_start = q_start;
+  s.vl_q_len = q_len;
+  s.vl_k_start = k_start;
+  s.vl_k_len = k_len;
+  s.vl_nseq = n_seq;
+  s.vl_tiles = (int32_t)tiles;
+  s.vl_nq = Nq;
+  s.vl_nk = Nk;
+  const FwdParams p = make_params(1, Hq, Hkv, Nq, Nk, resolve_scale(scale, d));
+  return dispatch(dtype, d, q, k, v, out, lse, false, p, s, (int64_t)s.n_tiles * Hq, stream);
+}
+
 extern "C" int rattn_fwd_split(const void* q, const void* k, const void* v, void* out,
                                float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d,
                                int dtype, float scale, int causal, int n_ring_steps, int zigzag,

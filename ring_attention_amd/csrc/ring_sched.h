@@ -31,6 +31,7 @@ enum VisitMode : int32_t {
   kVisitExplicit = 0,        // the launch lists its key/value runs (one ring step)
   kVisitContiguousRing = 1,  // rank r holds block r of W equal blocks
   kVisitZigZagRing = 2,      // rank r holds chunks r and 2W-1-r of 2W chunks
+  kVisitVarlen = 3,          // independent sequences of a packed batch
 };
 
 // A contiguous run of rows of a tensor: rows [row0, row0+len) sit at global
@@ -61,16 +62,45 @@ struct Sched {
   int32_t br;         // query rows per tile this schedule was built for
   Run kruns[2];
   QSeg qseg[kMaxQSeg];
+  // Varlen mode: sequence i owns query rows [vl_q_start[i], +vl_q_len[i]) and
+  // key/value rows [vl_k_start[i], +vl_k_len[i]) (device arrays of vl_nseq
+  // int32, clamped to the vl_nq / vl_nk rows the tensors hold); query tile t
+  // is tile t % vl_tiles of sequence t / vl_tiles.  Positions inside a
+  // sequence: key j at j, query i at len_k - len_q + i (the last query
+  // aligned with the last key).
+  const int32_t* vl_q_start;
+  const int32_t* vl_q_len;
+  const int32_t* vl_k_start;
+  const int32_t* vl_k_len;
+  int32_t vl_nseq;
+  int32_t vl_tiles;
+  int64_t vl_nq;
+  int64_t vl_nk;
 };
 
 RATTN_HD int32_t num_visits(const Sched& s) {
+  if (s.mode == kVisitVarlen) return 1;
   return s.mode == kVisitExplicit ? s.n_kruns : (s.mode == kVisitContiguousRing ? s.W : 2 * s.W);
 }
+
+#if defined(__HIPCC__)
+// Key/value rows of varlen sequence i, clamped to the rows k holds (device only).
+__device__ __forceinline__ Run varlen_keys(const Sched& s, int32_t i) {
+  const int64_t st = s.vl_k_start[i];
+  int64_t len = s.vl_k_len[i];
+  if (st < 0 || st > s.vl_nk) return Run{0, 0, 0};
+  if (len > s.vl_nk - st) len = s.vl_nk - st;
+  return Run{st, len < 0 ? 0 : len, 0};
+}
+#endif
 
 // Key/value run visited at position v of rank's ring order.  Outside explicit
 // mode the key/value tensor is in natural order, so row index == position.
 RATTN_HD Run visit(const Sched& s, int32_t rank, int32_t v) {
   Run r;
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (s.mode == kVisitVarlen) return varlen_keys(s, rank);  // rank = sequence
+#endif
   if (s.mode == kVisitExplicit) {
     r = s.kruns[v];
   } else if (s.mode == kVisitContiguousRing) {
@@ -111,6 +141,25 @@ struct QTile {
 
 RATTN_HD QTile query_tile(const Sched& s, int32_t t) {
   QTile qt;
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (s.mode == kVisitVarlen) {
+    // rows <= 0: a tile past the end of its sequence (the kernel exits)
+    const int32_t i = t / s.vl_tiles;
+    int64_t lt = t % s.vl_tiles;
+    const int64_t st = s.vl_q_start[i];
+    int64_t lq = s.vl_q_len[i];
+    if (st < 0 || st > s.vl_nq) lq = 0;
+    if (lq > s.vl_nq - st) lq = s.vl_nq - st;
+    const int64_t nt = (lq + s.br - 1) / s.br;
+    if (s.reverse) lt = nt - 1 - lt;  // causal: latest (longest) tiles first
+    qt.row0 = st + lt * s.br;
+    const int64_t rem = lq - lt * s.br;
+    qt.rows = (lt < 0 || lt >= nt) ? 0 : (rem < s.br ? rem : s.br);
+    qt.pos0 = varlen_keys(s, i).len - lq + lt * s.br;
+    qt.rank = i;
+    return qt;
+  }
+#endif
   int32_t i = 0;
   for (; i + 1 < s.n_qseg; ++i)
     if (t < s.qseg[i + 1].tile_begin) break;

@@ -252,3 +252,34 @@ def test_bwd_step_without_pairs_is_ok(rattn_lib):
 ])
 def test_bwd_delta_rejects(rattn_lib, args, status):
     assert rattn_lib.rattn_bwd_delta(*args, None) == status
+
+
+def fwd_varlen(lib, q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4], qs=P[5], ql=P[5] + 256,
+               ks=P[5] + 512, kl=P[5] + 768, n_seq=3, max_len_q=64, Nq=128, Nk=128, Hq=2,
+               Hkv=1, d=64, dtype=2, scale=0.0, causal=1):
+    return lib.rattn_fwd_varlen(q, k, v, out, lse, qs, ql, ks, kl, n_seq, max_len_q, Nq, Nk, Hq,
+                                Hkv, d, dtype, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), EINVAL), (dict(qs=0), EINVAL), (dict(kl=0), EINVAL), (dict(Hq=3, Hkv=2), EINVAL),
+    (dict(n_seq=-1), EINVAL), (dict(max_len_q=-5), EINVAL), (dict(d=48), EUNSUP),
+    (dict(dtype=7), EINVAL), (dict(causal=5), EINVAL), (dict(out=P[3] + 4), EINVAL),
+    (dict(ql=P[5] + 258), EINVAL), (dict(Nq=-1), EINVAL),
+])
+def test_fwd_varlen_rejects(rattn_lib, kw, status):
+    assert fwd_varlen(rattn_lib, **kw) == status
+
+
+def test_fwd_varlen_without_work_is_ok(rattn_lib):
+    assert fwd_varlen(rattn_lib, n_seq=0) == OK
+    assert fwd_varlen(rattn_lib, max_len_q=0) == OK
+    assert fwd_varlen(rattn_lib, q=0, out=0, lse=0, Nq=0) == OK
+
+
+def test_varlen_from_cu_seqlens():
+    assert binding.varlen_from_cu_seqlens([0, 3, 3, 10]) == ([0, 3, 3], [3, 0, 7])
+    with pytest.raises(ValueError):
+        binding.varlen_from_cu_seqlens([1, 3])
+    with pytest.raises(ValueError):
+        binding.varlen_from_cu_seqlens([0, 5, 4])
