@@ -302,28 +302,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
         lv[j] = *(const f32x4*)(lse_l + 32 * qb + 8 * j + 4 * hl);
         dv4[j] = *(const f32x4*)(dl_l + 32 * qb + 8 * j + 4 * hl);
       }
-      // visible iff the row exists and (causal) the key is not after it:
-      // row index - rel >= 0 with rel = kpos - (x.pos0 + 32 qb + 4 hl)
-      const int64_t rel64 = kpos - (x.pos0 + 32 * qb + 4 * hl);
-      const int rel = rel64 > 64 ? 64 : (rel64 < -64 ? -64 : (int)rel64);
-      const int rlim = x.rows - 32 * qb - 4 * hl;  // rows r2 < rlim exist
+      // P and dS of the block, each step over all 16 registers at once so
+      // that the independent chains overlap.  Register r of a lane holds
+      // query row 32 qb + 8 (r/4) + 4 hl + r%4, visible iff the row exists
+      // and (causal) the key is not after it: r2 = 8 (r/4) + r%4 in
+      // [rel, rlim) with rel = kpos - (x.pos0 + 32 qb + 4 hl).
+      float pr[16], ds[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        pr[rr] = fmaf(s_acc[rr], p.c, -lse2_of(lv[rr >> 2][rr & 3]));
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) pr[rr] = exp2_fast(pr[rr]);
+      if (need_mask) {
+        const int64_t rel64 = kpos - (x.pos0 + 32 * qb + 4 * hl);
+        const int rel = p.causal ? (rel64 > 64 ? 64 : (rel64 < -64 ? -64 : (int)rel64)) : -64;
+        const int rlim = x.rows - 32 * qb - 4 * hl;  // rows r2 < rlim exist
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int r2 = 8 * (rr >> 2) + (rr & 3);
+          pr[rr] = ((r2 >= rel) & (r2 < rlim)) ? pr[rr] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) ds[rr] = pr[rr] * (dp_acc[rr] - dv4[rr >> 2][rr & 3]);
       float pw[8], dw[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float pr[2], ds[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int rr = r + e;
-          const int r2 = 8 * (rr >> 2) + (rr & 3);
-          const float l2 = lse2_of(lv[rr >> 2][rr & 3]);
-          bool vis = true;
-          if (need_mask) vis = r2 < rlim && (!p.causal || r2 >= rel);
-          const float x2 = exp2_fast(fmaf(s_acc[rr], p.c, -l2));
-          pr[e] = vis ? x2 : 0.f;
-          ds[e] = pr[e] * (dp_acc[rr] - dv4[rr >> 2][rr & 3]);
-        }
-        pack_pair<TT>(&pw[r >> 1], pr[0], pr[1]);
-        pack_pair<TT>(&dw[r >> 1], ds[0], ds[1]);
+        pack_pair<TT>(&pw[r >> 1], pr[r], pr[r + 1]);
+        pack_pair<TT>(&dw[r >> 1], ds[r], ds[r + 1]);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -484,22 +490,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
     // below lim are visible to this lane's query
     const int lim =
         (need_mask ? visible_limit(x.rows, p.causal, qpos - x.pos0) : kRows) - 4 * hl;
+    // dS of each block, each step over its 16 registers at once so that the
+    // independent chains overlap
     float dw[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float ds[2];
+      for (int rr = 0; rr < 16; ++rr) ds[rr] = exp2_fast(fmaf(s_acc[kb][rr], p.c, -l2));
+      if (need_mask) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int rr = r + e;
+        for (int rr = 0; rr < 16; ++rr) {
           const int kk2 = 32 * kb + 8 * (rr >> 2) + (rr & 3);
-          const float x2 = exp2_fast(fmaf(s_acc[kb][rr], p.c, -l2));
-          const float pr = kk2 < lim ? x2 : 0.f;
-          ds[e] = pr * (dp_acc[kb][rr] - dl);
+          ds[rr] = kk2 < lim ? ds[rr] : 0.f;
         }
-        pack_pair<TT>(&dw[8 * kb + (r >> 1)], ds[0], ds[1]);
       }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) ds[rr] *= dp_acc[kb][rr] - dl;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) pack_pair<TT>(&dw[8 * kb + (r >> 1)], ds[r], ds[r + 1]);
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const v8 du = packed_operand<TT>(dw, u);
