@@ -250,8 +250,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
   };
   auto tile_of = [&](int64_t t) {
     QT x;
-    const int64_t g = t / per_head;
-    int64_t r = t - g * per_head;
+    // 32-bit: a workgroup walks far fewer than 2^31 tiles
+    const int32_t g = (int32_t)((uint32_t)t / (uint32_t)per_head);
+    int64_t r = t - (int64_t)g * per_head;
     const int ri = r < nt[0] ? 0 : 1;
     if (ri) r -= nt[0];
     const int64_t i0 = st[ri] + r * kRows;
