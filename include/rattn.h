@@ -224,6 +224,24 @@ RATTN_API int rattn_bwd(const void* q, const void* k, const void* v, const void*
                         int rank, void* stream);
 
 /*
+ * Backward of rattn_fwd_varlen: sequence i (query rows [q_start[i],
+ * +q_len[i]) of q, out, dout [Nq, Hq, d]; key rows [k_start[i], +k_len[i])
+ * of k, v [Nk, Hkv, d]; positions as rattn_fwd_varlen) gets its gradients
+ * from its own pairs only.  dq [Nq, Hq, d], dk, dv [Nk, Hkv, d] in the input
+ * type are written on the rows of the sequences (other rows untouched);
+ * delta_ws: caller scratch of Nq*Hq float32.  q_start .. k_len are DEVICE
+ * arrays of n_seq int32 (clamped as in rattn_fwd_varlen); max_len_q,
+ * max_len_k bound the lengths.  Other arguments and errors as rattn_bwd.
+ */
+RATTN_API int rattn_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               float* delta_ws, const int32_t* q_start, const int32_t* q_len,
+                               const int32_t* k_start, const int32_t* k_len, int n_seq,
+                               int64_t max_len_q, int64_t max_len_k, int64_t Nq, int64_t Nk,
+                               int Hq, int Hkv, int d, int dtype, float scale, int causal,
+                               void* stream);
+
+/*
  * One ring step of the backward: the pairs between query rows
  * [q_off, q_off + Nq) of a [B, q_rows, Hq, .] row space (q, dout dtype
  * [.., d]; lse, delta float32 [B, q_rows, Hq]; dq_acc float32 [.., d]) and

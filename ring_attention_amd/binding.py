@@ -22,7 +22,7 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 # Exported symbols, in the order include/rattn.h declares them.
 EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_fwd_step_merge", "rattn_merge",
            "rattn_fwd_varlen", "rattn_fwd_split", "rattn_split_hint", "rattn_bwd_delta",
-           "rattn_bwd", "rattn_bwd_step", "rattn_status_string")
+           "rattn_bwd", "rattn_bwd_varlen", "rattn_bwd_step", "rattn_status_string")
 
 
 class RattnError(RuntimeError):
@@ -71,6 +71,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rattn_bwd.restype = i32
     lib.rattn_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i64, i64, i32, i32, f32, i32, i32, i32,
                                           i32, vp]
+    lib.rattn_bwd_varlen.restype = i32
+    lib.rattn_bwd_varlen.argtypes = [vp] * 14 + [i32, i64, i64, i64, i64, i32, i32, i32, i32,
+                                                 f32, i32, vp]
     lib.rattn_bwd_step.restype = i32
     lib.rattn_bwd_step.argtypes = [vp] * 9 + [i32, i32, i32, i64, i64, i64, i64, i64, i64, i32,
                                               i32, f32, i32, i64p, i64p, i64p, i64p, vp]
@@ -371,6 +374,51 @@ def varlen_from_cu_seqlens(cu_seqlens):
     return cu[:-1], [b - a for a, b in zip(cu, cu[1:])]
 
 
+def _varlen_ranges(q, k, q_start, q_len, k_start, k_len):
+    """Checked host ranges and their int32 device copies."""
+    Nq, Nk = q.shape[0], k.shape[0]
+    ranges = [list(map(int, x)) for x in (q_start, q_len, k_start, k_len)]
+    n_seq = len(ranges[0])
+    if any(len(x) != n_seq for x in ranges):
+        raise ValueError("q_start, q_len, k_start, k_len must have one entry per sequence")
+    for (qs, ql, ks, kl) in zip(*ranges):
+        if qs < 0 or ql < 0 or qs + ql > Nq or ks < 0 or kl < 0 or ks + kl > Nk:
+            raise ValueError("a sequence range lies outside q or k")
+    dev = [torch.tensor(x if x else [0], dtype=torch.int32, device=q.device) for x in ranges]
+    return ranges, n_seq, dev
+
+
+def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+               lse: torch.Tensor, dout: torch.Tensor, q_start, q_len, k_start, k_len,
+               causal: bool = False, scale: float | None = None):
+    """Backward of ``fwd_varlen`` (rattn_bwd_varlen): returns (dq, dk, dv) in
+    q's dtype, zero on rows outside every sequence."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3 or not t.is_cuda or \
+                not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D GPU tensor [N, H, d]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or \
+            q.dtype not in DTYPE_CODES or k.shape != v.shape or out.shape != q.shape or \
+            dout.shape != q.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("q, out, dout [Nq, Hq, d] and k, v [Nk, Hkv, d] of one dtype")
+    Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[0], k.shape[1]
+    _like("lse", lse, q, torch.float32)
+    if lse.shape != (Nq, Hq):
+        raise ValueError("lse must be [Nq, Hq]")
+    ranges, n_seq, dev = _varlen_ranges(q, k, q_start, q_len, k_start, k_len)
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    ws = torch.empty((Nq, Hq), dtype=torch.float32, device=q.device)
+    rc = load_library().rattn_bwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+        *[t.data_ptr() for t in dev], n_seq, max(ranges[1], default=0),
+        max(ranges[3], default=0), Nq, Nk, Hq, Hkv, d, DTYPE_CODES[q.dtype], _scale(scale),
+        int(bool(causal)), _stream(q))
+    _check("rattn_bwd_varlen", rc)
+    return dq, dk, dv
+
+
 def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_start, q_len, k_start,
                k_len, causal: bool = False, scale: float | None = None,
                out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
@@ -389,13 +437,7 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_start, q_len
         raise ValueError("q, k, v must share dtype and head dim; k, v one shape")
     Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[0], k.shape[1]
-    ranges = [list(map(int, x)) for x in (q_start, q_len, k_start, k_len)]
-    n_seq = len(ranges[0])
-    if any(len(x) != n_seq for x in ranges):
-        raise ValueError("q_start, q_len, k_start, k_len must have one entry per sequence")
-    for (qs, ql, ks, kl) in zip(*ranges):
-        if qs < 0 or ql < 0 or qs + ql > Nq or ks < 0 or kl < 0 or ks + kl > Nk:
-            raise ValueError("a sequence range lies outside q or k")
+    ranges, n_seq, dev = _varlen_ranges(q, k, q_start, q_len, k_start, k_len)
     if out is None:
         out = torch.zeros_like(q)
     if lse is None:
@@ -404,7 +446,6 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_start, q_len
     _like("lse", lse, q, torch.float32)
     if out.shape != q.shape or lse.shape != (Nq, Hq):
         raise ValueError("out must be [Nq, Hq, d] and lse [Nq, Hq]")
-    dev = [torch.tensor(x if x else [0], dtype=torch.int32, device=q.device) for x in ranges]
     max_len_q = max(ranges[1]) if n_seq else 0
     rc = load_library().rattn_fwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),

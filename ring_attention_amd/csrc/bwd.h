@@ -41,6 +41,18 @@ struct BwdParams {
   int32_t nq, nk;         // runs in use (1 or 2 each)
   BwdRun q[2], k[2];
   int32_t accumulate;     // 1: fp32 outputs, added to; 0: outputs in the input type
+  // Varlen (vl_nseq > 0; B = 1, offsets 0): sequence i owns query rows
+  // [vl_q_start[i], +vl_q_len[i]) and key rows [vl_k_start[i], +vl_k_len[i])
+  // (device arrays, clamped to q_rows / k_rows), key j at position j, query
+  // i at k_len - q_len + i; the runs above are unused.  vl_max_q / vl_max_k
+  // bound the lengths (tiles per sequence).
+  const int32_t* vl_q_start;
+  const int32_t* vl_q_len;
+  const int32_t* vl_k_start;
+  const int32_t* vl_k_len;
+  int32_t vl_nseq;
+  int64_t vl_max_q;
+  int64_t vl_max_k;
 };
 
 // Tile of `br` rows number t over one side's runs (tiles do not straddle runs).
@@ -67,6 +79,84 @@ __host__ __device__ __forceinline__ BwdTile bwd_tile(const BwdRun* r, int n, int
   }
   return x;
 }
+
+// Work items of the query-stationary (dQ) and key-stationary (dK/dV)
+// kernels: tiles of `br` rows of one side, numbered over the runs, or over
+// (sequence, tile) in varlen mode.
+__host__ __device__ __forceinline__ int64_t bwd_q_tiles(const BwdParams& p, int br) {
+  return p.vl_nseq > 0 ? p.vl_nseq * ((p.vl_max_q + br - 1) / br) : bwd_tiles(p.q, p.nq, br);
+}
+__host__ __device__ __forceinline__ int64_t bwd_k_tiles(const BwdParams& p, int br) {
+  return p.vl_nseq > 0 ? p.vl_nseq * ((p.vl_max_k + br - 1) / br) : bwd_tiles(p.k, p.nk, br);
+}
+
+// One work item: its tile (rows <= 0: nothing to do) and the runs of the
+// other side it pairs with.
+struct BwdItem {
+  BwdTile tile;
+  BwdRun other[2];
+  int n_other;
+};
+
+#if defined(__HIPCC__)
+__device__ __forceinline__ void bwd_seq(const BwdParams& p, int32_t i, int64_t* qs, int64_t* lq,
+                                        int64_t* ks, int64_t* lk) {
+  *qs = p.vl_q_start[i];
+  *lq = p.vl_q_len[i];
+  *ks = p.vl_k_start[i];
+  *lk = p.vl_k_len[i];
+  if (*qs < 0 || *qs > p.q_rows) *lq = 0;
+  if (*lq > p.q_rows - *qs) *lq = p.q_rows - *qs;
+  if (*lq < 0) *lq = 0;
+  if (*ks < 0 || *ks > p.k_rows) *lk = 0;
+  if (*lk > p.k_rows - *ks) *lk = p.k_rows - *ks;
+  if (*lk < 0) *lk = 0;
+}
+
+__device__ __forceinline__ BwdItem bwd_q_item(const BwdParams& p, int br, int64_t t) {
+  BwdItem it;
+  if (p.vl_nseq <= 0) {
+    it.tile = bwd_tile(p.q, p.nq, br, t);
+    it.n_other = p.nk;
+    it.other[0] = p.k[0];
+    it.other[1] = p.k[1];
+    return it;
+  }
+  const int64_t per = (p.vl_max_q + br - 1) / br;
+  const int32_t i = (int32_t)(t / per);
+  const int64_t lt = t - (int64_t)i * per;
+  int64_t qs, lq, ks, lk;
+  bwd_seq(p, i, &qs, &lq, &ks, &lk);
+  const int64_t rem = lq - lt * br;
+  it.tile = BwdTile{qs + lt * br, rem <= 0 ? 0 : (rem < br ? rem : br), lk - lq + lt * br};
+  it.other[0] = BwdRun{ks, lk, 0};
+  it.other[1] = BwdRun{0, 0, 0};
+  it.n_other = lk > 0 ? 1 : 0;
+  return it;
+}
+
+__device__ __forceinline__ BwdItem bwd_k_item(const BwdParams& p, int br, int64_t t) {
+  BwdItem it;
+  if (p.vl_nseq <= 0) {
+    it.tile = bwd_tile(p.k, p.nk, br, t);
+    it.n_other = p.nq;
+    it.other[0] = p.q[0];
+    it.other[1] = p.q[1];
+    return it;
+  }
+  const int64_t per = (p.vl_max_k + br - 1) / br;
+  const int32_t i = (int32_t)(t / per);
+  const int64_t lt = t - (int64_t)i * per;
+  int64_t qs, lq, ks, lk;
+  bwd_seq(p, i, &qs, &lq, &ks, &lk);
+  const int64_t rem = lk - lt * br;
+  it.tile = BwdTile{ks + lt * br, rem <= 0 ? 0 : (rem < br ? rem : br), lt * br};
+  it.other[0] = BwdRun{qs, lq, lk - lq};
+  it.other[1] = BwdRun{0, 0, 0};
+  it.n_other = lq > 0 ? 1 : 0;
+  return it;
+}
+#endif
 
 // D = rowsum(dO * O) in float32 for `rows` rows of d elements (input type).
 hipError_t launch_bwd_delta(int dtype, int d, const void* out, const void* dout, float* delta,

@@ -100,7 +100,9 @@ __global__ __launch_bounds__(256) void bwd_dq_generic_kernel(
   const int32_t bh = blockIdx.x % BH;
   const int64_t tl = blockIdx.x / BH;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
-  const BwdTile qt = bwd_tile(p.q, p.nq, RQ, tl);
+  const BwdItem item = bwd_q_item(p, RQ, tl);
+  if (item.tile.rows <= 0) return;  // varlen: a tile past the end of its sequence
+  const BwdTile qt = item.tile;
   const int r = threadIdx.x / S::LP, part = threadIdx.x % S::LP;
   const bool valid = r < qt.rows;
   const int64_t qpos = qt.pos0 + r;
@@ -119,8 +121,8 @@ __global__ __launch_bounds__(256) void bwd_dq_generic_kernel(
   const bool live = lse2 != kNegInf;  // a row that saw no key has P = 0 everywhere
 
   const int64_t kstride = (int64_t)p.Hkv * D;
-  for (int ri = 0; ri < p.nk; ++ri) {
-    const Run run{p.k[ri].row0, p.k[ri].len, p.k[ri].pos0};
+  for (int ri = 0; ri < item.n_other; ++ri) {
+    const Run run{item.other[ri].row0, item.other[ri].len, item.other[ri].pos0};
     const int64_t nt = live_tiles(run, qhi, p.causal, BC);
     for (int64_t t = 0; t < nt; ++t) {
       const int64_t krow0 = p.k_off + run.row0 + t * BC;
@@ -179,7 +181,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_generic_kernel(
   const int32_t bh = blockIdx.x % BH;
   const int64_t tl = blockIdx.x / BH;
   const int32_t b = bh / p.Hkv, hkv = bh % p.Hkv;
-  const BwdTile kt = bwd_tile(p.k, p.nk, RK, tl);
+  const BwdItem item = bwd_k_item(p, RK, tl);
+  if (item.tile.rows <= 0) return;  // varlen: a tile past the end of its sequence
+  const BwdTile kt = item.tile;
   const int r = threadIdx.x / S::LP, part = threadIdx.x % S::LP;
   const bool valid = r < kt.rows;
   const int64_t kpos = kt.pos0 + r;
@@ -196,8 +200,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_generic_kernel(
   const int64_t qstride = (int64_t)p.Hq * D;
   for (int g = 0; g < p.group; ++g) {
     const int32_t hq = hkv * p.group + g;
-    for (int ri = 0; ri < p.nq; ++ri) {
-      const BwdRun run = p.q[ri];
+    for (int ri = 0; ri < item.n_other; ++ri) {
+      const BwdRun run = item.other[ri];
       // query rows before the tile's first key position see none of its keys
       int64_t start = 0;
       if (p.causal) {
@@ -290,7 +294,7 @@ hipError_t generic_acc(const void* q, const void* k, const void* v, const void* 
                        const BwdParams& p, hipStream_t stream) {
   using E = typename TT::elem;
   using S = RowSplit<D>;
-  const int64_t qb = bwd_tiles(p.q, p.nq, 256 / S::LP) * p.B * p.Hq;
+  const int64_t qb = bwd_q_tiles(p, 256 / S::LP) * p.B * p.Hq;
   if (qb > 0) {
     hipLaunchKernelGGL((bwd_dq_generic_kernel<TT, D, ACC>), dim3((unsigned)qb), dim3(256), 0,
                        stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,
@@ -298,7 +302,7 @@ hipError_t generic_acc(const void* q, const void* k, const void* v, const void* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t kb = bwd_tiles(p.k, p.nk, 256 / S::LP) * p.B * p.Hkv;
+  const int64_t kb = bwd_k_tiles(p, 256 / S::LP) * p.B * p.Hkv;
   if (kb > 0) {
     hipLaunchKernelGGL((bwd_dkv_generic_kernel<TT, D, ACC>), dim3((unsigned)kb), dim3(256), 0,
                        stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,

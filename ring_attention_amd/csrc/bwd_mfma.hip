@@ -201,9 +201,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
   const int32_t BH = p.B * p.Hkv;
   int32_t bh;
   int64_t tl;
-  work_order(BH, bwd_tiles(p.k, p.nk, kOwn), false, &bh, &tl);
+  work_order(BH, bwd_k_tiles(p, kOwn), false, &bh, &tl);
   const int32_t b = bh / p.Hkv, hkv = bh % p.Hkv;
-  const BwdTile kt = bwd_tile(p.k, p.nk, kOwn, tl);
+  const BwdItem item = bwd_k_item(p, kOwn, tl);
+  if (item.tile.rows <= 0) return;  // varlen: a tile past the end of its sequence
+  const BwdTile kt = item.tile;
+  const BwdRun* qrun = item.other;
   const int wk0 = 32 * wave;
   const int wkrows = kt.rows - wk0 < 0 ? 0 : (kt.rows - wk0 > 32 ? 32 : (int)(kt.rows - wk0));
   const bool k_valid = l32 < wkrows;
@@ -231,14 +234,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
   // query tiles: every head of the group, each run from the first row that
   // can see one of this workgroup's keys
   int64_t st[2] = {0, 0}, nt[2] = {0, 0};
-  for (int ri = 0; ri < p.nq; ++ri) {
+  for (int ri = 0; ri < item.n_other; ++ri) {
     int64_t s0 = 0;
     if (p.causal) {
-      s0 = kt.pos0 - p.q[ri].pos0;
-      s0 = s0 < 0 ? 0 : (s0 > p.q[ri].len ? p.q[ri].len : s0);
+      s0 = kt.pos0 - qrun[ri].pos0;
+      s0 = s0 < 0 ? 0 : (s0 > qrun[ri].len ? qrun[ri].len : s0);
     }
     st[ri] = s0;
-    nt[ri] = (p.q[ri].len - s0 + kRows - 1) / kRows;
+    nt[ri] = (qrun[ri].len - s0 + kRows - 1) / kRows;
   }
   const int64_t per_head = nt[0] + nt[1];
   const int64_t T = per_head * p.group;
@@ -256,10 +259,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
     const int ri = r < nt[0] ? 0 : 1;
     if (ri) r -= nt[0];
     const int64_t i0 = st[ri] + r * kRows;
-    const int64_t rem = p.q[ri].len - i0;
+    const int64_t rem = qrun[ri].len - i0;
     x.rows = rem < kRows ? (int)rem : kRows;
-    x.row0 = (int64_t)b * p.q_rows + p.q_off + p.q[ri].row0 + i0;
-    x.pos0 = p.q[ri].pos0 + i0;
+    x.row0 = (int64_t)b * p.q_rows + p.q_off + qrun[ri].row0 + i0;
+    x.pos0 = qrun[ri].pos0 + i0;
     x.hq = hkv * p.group + (int32_t)g;
     return x;
   };
@@ -410,9 +413,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
   const int32_t BH = p.B * p.Hq;
   int32_t bh;
   int64_t tl;
-  work_order(BH, bwd_tiles(p.q, p.nq, kOwn), p.causal != 0, &bh, &tl);
+  work_order(BH, bwd_q_tiles(p, kOwn), p.causal != 0, &bh, &tl);
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
-  const BwdTile qt = bwd_tile(p.q, p.nq, kOwn, tl);
+  const BwdItem item = bwd_q_item(p, kOwn, tl);
+  if (item.tile.rows <= 0) return;  // varlen: a tile past the end of its sequence
+  const BwdTile qt = item.tile;
+  const BwdRun* krun = item.other;
   const int wq0 = 32 * wave;
   const int wqrows = qt.rows - wq0 < 0 ? 0 : (qt.rows - wq0 > 32 ? 32 : (int)(qt.rows - wq0));
   const bool q_valid = l32 < wqrows;
@@ -442,8 +448,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
 
   // key tiles: the live prefix of every key run
   int64_t nt[2] = {0, 0};
-  for (int ri = 0; ri < p.nk; ++ri)
-    nt[ri] = live_tiles(Run{p.k[ri].row0, p.k[ri].len, p.k[ri].pos0}, qhi, p.causal, kRows);
+  for (int ri = 0; ri < item.n_other; ++ri)
+    nt[ri] = live_tiles(Run{krun[ri].row0, krun[ri].len, krun[ri].pos0}, qhi, p.causal, kRows);
   const int64_t T = nt[0] + nt[1];
   struct KT {
     int64_t row0;
@@ -454,10 +460,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
     KT x;
     const int ri = t < nt[0] ? 0 : 1;
     const int64_t tt = ri ? t - nt[0] : t;
-    const int64_t rem = p.k[ri].len - tt * kRows;
+    const int64_t rem = krun[ri].len - tt * kRows;
     x.rows = rem < kRows ? (int)rem : kRows;
-    x.row0 = (int64_t)b * p.k_rows + p.k_off + p.k[ri].row0 + tt * kRows;
-    x.pos0 = p.k[ri].pos0 + tt * kRows;
+    x.row0 = (int64_t)b * p.k_rows + p.k_off + krun[ri].row0 + tt * kRows;
+    x.pos0 = krun[ri].pos0 + tt * kRows;
     return x;
   };
   const int64_t kstride = (int64_t)p.Hkv * D;
@@ -558,7 +564,7 @@ hipError_t launch_acc(const void* q, const void* k, const void* v, const void* d
                       const float* lse, const float* delta, void* dq, void* dk, void* dv,
                       const BwdParams& p, hipStream_t stream) {
   using E = typename TT::elem;
-  const int64_t qb = bwd_tiles(p.q, p.nq, kOwn) * p.B * p.Hq;
+  const int64_t qb = bwd_q_tiles(p, kOwn) * p.B * p.Hq;
   if (qb > 0) {
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<TT, ACC>), dim3((unsigned)qb), dim3(kThreads), 0,
                        stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,
@@ -566,7 +572,7 @@ hipError_t launch_acc(const void* q, const void* k, const void* v, const void* d
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t kb = bwd_tiles(p.k, p.nk, kOwn) * p.B * p.Hkv;
+  const int64_t kb = bwd_k_tiles(p, kOwn) * p.B * p.Hkv;
   if (kb > 0) {
     hipLaunchKernelGGL((bwd_dkv_mfma_kernel<TT, ACC>), dim3((unsigned)kb), dim3(kThreads), 0,
                        stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,

@@ -399,8 +399,8 @@ void set_runs(BwdRun* dst, int32_t* n, const BwdRun* src, int m) {
 int bwd_dispatch(int dtype, int d, const void* q, const void* k, const void* v,
                  const void* dout, const float* lse, const float* delta, void* dq, void* dk,
                  void* dv, const BwdParams& p, void* stream) {
-  const int64_t g1 = bwd_tiles(p.q, p.nq, 64) * p.B * p.Hq;
-  const int64_t g2 = bwd_tiles(p.k, p.nk, 64) * p.B * p.Hkv;
+  const int64_t g1 = bwd_q_tiles(p, 64) * p.B * p.Hq;
+  const int64_t g2 = bwd_k_tiles(p, 64) * p.B * p.Hkv;
   if (g1 > INT32_MAX || g2 > INT32_MAX) return RATTN_EUNSUPPORTED;
   hipError_t e =
       (dtype != RATTN_F32 && d == 128)
@@ -475,6 +475,49 @@ extern "C" int rattn_bwd(const void* q, const void* k, const void* v, const void
   if (Nq > 0) {
     hipError_t e = launch_bwd_delta(dtype, d, out, dout, delta_ws, (int64_t)B * Nq * Hq,
                                     (hipStream_t)stream);
+    if (e != hipSuccess) return RATTN_EHIP;
+  }
+  return bwd_dispatch(dtype, d, q, k, v, dout, lse, delta_ws, dq, dk, dv, p, stream);
+}
+
+extern "C" int rattn_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                                const float* lse, const void* dout, void* dq, void* dk,
+                                void* dv, float* delta_ws, const int32_t* q_start,
+                                const int32_t* q_len, const int32_t* k_start,
+                                const int32_t* k_len, int n_seq, int64_t max_len_q,
+                                int64_t max_len_k, int64_t Nq, int64_t Nk, int Hq, int Hkv,
+                                int d, int dtype, float scale, int causal, void* stream) {
+  using namespace rattn;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
+  if (n_seq < 0 || max_len_q < 0 || max_len_k < 0 || Nq < 0 || Nk < 0) return RATTN_EINVAL;
+  int rc = check_dtype_d(dtype, d);
+  if (rc != RATTN_OK) return rc;
+  if (causal != 0 && causal != 1) return RATTN_EINVAL;
+  if (n_seq == 0 || (Nq == 0 && Nk == 0)) return RATTN_OK;
+  if ((Nq > 0 && (!q || !out || !lse || !dout || !dq || !delta_ws)) ||
+      (Nk > 0 && (!k || !v || !dk || !dv)) || !q_start || !q_len || !k_start || !k_len)
+    return RATTN_EINVAL;
+  const void* p16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* x : p16)
+    if (!aligned(x, 16)) return RATTN_EINVAL;
+  if (!aligned(lse, 4) || !aligned(delta_ws, 4) || !aligned(q_start, 4) ||
+      !aligned(q_len, 4) || !aligned(k_start, 4) || !aligned(k_len, 4))
+    return RATTN_EINVAL;
+  if (!tensor_ok(1, std::max(Nq, Nk), Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
+  if (max_len_q > INT32_MAX || max_len_k > INT32_MAX) return RATTN_EUNSUPPORTED;
+  BwdParams p = make_bwd_params(1, Hq, Hkv, resolve_scale(scale, d));
+  p.causal = causal;
+  p.q_rows = Nq;
+  p.k_rows = Nk;
+  p.vl_q_start = q_start;
+  p.vl_q_len = q_len;
+  p.vl_k_start = k_start;
+  p.vl_k_len = k_len;
+  p.vl_nseq = n_seq;
+  p.vl_max_q = max_len_q;
+  p.vl_max_k = max_len_k;
+  if (Nq > 0) {
+    hipError_t e = launch_bwd_delta(dtype, d, out, dout, delta_ws, Nq * Hq, (hipStream_t)stream);
     if (e != hipSuccess) return RATTN_EHIP;
   }
   return bwd_dispatch(dtype, d, q, k, v, dout, lse, delta_ws, dq, dk, dv, p, stream);

@@ -283,3 +283,27 @@ def test_varlen_from_cu_seqlens():
         binding.varlen_from_cu_seqlens([1, 3])
     with pytest.raises(ValueError):
         binding.varlen_from_cu_seqlens([0, 5, 4])
+
+
+def bwd_varlen(lib, q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4], dout=P[5], dq=P[6], dk=P[7],
+               dv=P[7] + 0x100000, ws=P[7] + 0x200000, qs=P[5] + 256, ql=P[5] + 512,
+               ks=P[5] + 768, kl=P[5] + 1024, n_seq=3, max_q=64, max_k=64, Nq=128, Nk=128,
+               Hq=2, Hkv=1, d=64, dtype=2, scale=0.0, causal=1):
+    return lib.rattn_bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, ws, qs, ql, ks, kl, n_seq,
+                                max_q, max_k, Nq, Nk, Hq, Hkv, d, dtype, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), EINVAL), (dict(dq=0), EINVAL), (dict(ws=0), EINVAL), (dict(kl=0), EINVAL),
+    (dict(Hq=3, Hkv=2), EINVAL), (dict(n_seq=-2), EINVAL), (dict(max_k=-1), EINVAL),
+    (dict(d=100), EUNSUP), (dict(dtype=9), EINVAL), (dict(causal=4), EINVAL),
+    (dict(dk=P[7] + 2), EINVAL), (dict(qs=P[5] + 258), EINVAL),
+    (dict(max_q=1 << 40), EUNSUP),
+])
+def test_bwd_varlen_rejects(rattn_lib, kw, status):
+    assert bwd_varlen(rattn_lib, **kw) == status
+
+
+def test_bwd_varlen_without_work_is_ok(rattn_lib):
+    assert bwd_varlen(rattn_lib, n_seq=0) == OK
+    assert bwd_varlen(rattn_lib, Nq=0, Nk=0) == OK

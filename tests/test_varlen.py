@@ -1,4 +1,5 @@
-"""Variable-length batches (rattn_fwd_varlen) vs the fp64 oracle (needs a GPU).
+"""Variable-length batches (rattn_fwd_varlen, rattn_bwd_varlen) vs the fp64
+oracle (needs a GPU).
 
 Each sequence is checked on its own against the oracle, with the positions
 the boundary documents (key j at j, query i at k_len - q_len + i); rows
@@ -113,3 +114,66 @@ def test_varlen_one_sequence_equals_fwd(gpu):
     o2, l2 = binding.fwd(qd[None], kd[None], vd[None], causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2[0]) and torch.equal(l1, l2[0])
+
+
+# --------------------------------------------------------------------------
+# backward (rattn_bwd_varlen)
+
+TOL_G = {torch.float32: 1e-4, torch.float16: 2e-2, torch.bfloat16: 2e-2}
+
+
+def check_bwd(q, k, v, do, grads, qs, ql, ks, kl, causal, dtype, what):
+    dq, dk, dv = (host(t) for t in grads)
+    for i, (a, n, b, m) in enumerate(zip(qs, ql, ks, kl)):
+        if n == 0 and m == 0:
+            continue
+        qpos = np.arange(n) + (m - n)
+        rq, rk, rv, _, _ = oracle.attention_bwd(q[None, a:a + n], k[None, b:b + m],
+                                                v[None, b:b + m], do[None, a:a + n],
+                                                causal=causal, q_pos=qpos, k_pos=np.arange(m))
+        for name, got, ref in (("dq", dq[a:a + n], rq[0]), ("dk", dk[b:b + m], rk[0]),
+                               ("dv", dv[b:b + m], rv[0])):
+            if ref.size == 0:
+                continue
+            err = float(np.abs(got - ref).max())
+            bar = TOL_G[dtype] * max(1.0, float(np.abs(ref).max()))
+            assert err <= bar, f"{what} seq {i} {name}: {err} > {bar}"
+    note(f"{what}: every sequence within its bar")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)],
+                         ids=["bf16_d128", "f32_d64"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_varlen_backward_packed(gpu, dtype, d, causal):
+    lens = [1, 70, 300, 0, 129, 511]
+    q, k, v = packed_inputs(lens, 4, 2, d, dtype, seed=450 + d)
+    N = sum(lens)
+    do = workloads.randn((N, 4, d), dtype, torch.Generator().manual_seed(451), "cpu")
+    starts, ls = binding.varlen_from_cu_seqlens(np.concatenate([[0], np.cumsum(lens)]))
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    out, lse = binding.fwd_varlen(qd, kd, vd, starts, ls, starts, ls, causal=causal)
+    grads = binding.bwd_varlen(qd, kd, vd, out, lse, dod, starts, ls, starts, ls, causal=causal)
+    torch.cuda.synchronize()
+    check_bwd(q, k, v, do, grads, starts, ls, starts, ls, causal, dtype,
+              f"varlen bwd {dtype} d={d} causal={causal}")
+
+
+def test_varlen_backward_padded_and_cross_lengths(gpu):
+    """Padded blocks (pad rows get no gradient) and q_len != k_len."""
+    dtype, d = torch.bfloat16, 128
+    S = 256
+    ql, kl = [256, 17, 100], [256, 40, 7]
+    qs, ks = [0, S, 2 * S], [0, S, 2 * S]
+    q, k, v = packed_inputs([3 * S], 2, 2, d, dtype, seed=460)
+    do = workloads.randn((3 * S, 2, d), dtype, torch.Generator().manual_seed(461), "cpu")
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    out, lse = binding.fwd_varlen(qd, kd, vd, qs, ql, ks, kl, causal=True)
+    grads = binding.bwd_varlen(qd, kd, vd, out, lse, dod, qs, ql, ks, kl, causal=True)
+    torch.cuda.synchronize()
+    check_bwd(q, k, v, do, grads, qs, ql, ks, kl, True, dtype, "varlen bwd padded")
+    dq, dk, dv = (host(t) for t in grads)
+    for s0, n, m in zip(qs, ql, kl):
+        assert np.all(dq[s0 + n:s0 + S] == 0)
+        assert np.all(dk[s0 + m:s0 + S] == 0) and np.all(dv[s0 + m:s0 + S] == 0)
