@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256) void bwd_dq_generic_kernel(
 
   const int64_t kstride = (int64_t)p.Hkv * D;
   for (int ri = 0; ri < item.n_other; ++ri) {
-    const Run run{item.other[ri].row0, item.other[ri].len, item.other[ri].pos0};
+    const BwdRun r = ri == 0 ? item.other[0] : item.other[1];  // no runtime-indexed array
+    const Run run{r.row0, r.len, r.pos0};
     const int64_t nt = live_tiles(run, qhi, p.causal, BC);
     for (int64_t t = 0; t < nt; ++t) {
       const int64_t krow0 = p.k_off + run.row0 + t * BC;
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_generic_kernel(
   for (int g = 0; g < p.group; ++g) {
     const int32_t hq = hkv * p.group + g;
     for (int ri = 0; ri < item.n_other; ++ri) {
-      const BwdRun run = item.other[ri];
+      const BwdRun run = ri == 0 ? item.other[0] : item.other[1];
       // query rows before the tile's first key position see none of its keys
       int64_t start = 0;
       if (p.causal) {

@@ -206,7 +206,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
   const BwdItem item = bwd_k_item(p, kOwn, tl);
   if (item.tile.rows <= 0) return;  // varlen: a tile past the end of its sequence
   const BwdTile kt = item.tile;
-  const BwdRun* qrun = item.other;
+  // the (at most two) query runs as scalars: a runtime-indexed array would
+  // live in scratch, and the compiler's wait for a scratch load would also
+  // wait for the tile DMA issued before it
+  const BwdRun qr0 = item.other[0], qr1 = item.other[1];
   const int wk0 = 32 * wave;
   const int wkrows = kt.rows - wk0 < 0 ? 0 : (kt.rows - wk0 > 32 ? 32 : (int)(kt.rows - wk0));
   const bool k_valid = l32 < wkrows;
@@ -233,17 +236,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
 
   // query tiles: every head of the group, each run from the first row that
   // can see one of this workgroup's keys
-  int64_t st[2] = {0, 0}, nt[2] = {0, 0};
-  for (int ri = 0; ri < item.n_other; ++ri) {
+  auto run_start = [&](const BwdRun& r) {
     int64_t s0 = 0;
     if (p.causal) {
-      s0 = kt.pos0 - qrun[ri].pos0;
-      s0 = s0 < 0 ? 0 : (s0 > qrun[ri].len ? qrun[ri].len : s0);
+      s0 = kt.pos0 - r.pos0;
+      s0 = s0 < 0 ? 0 : (s0 > r.len ? r.len : s0);
     }
-    st[ri] = s0;
-    nt[ri] = (qrun[ri].len - s0 + kRows - 1) / kRows;
-  }
-  const int64_t per_head = nt[0] + nt[1];
+    return s0;
+  };
+  const int64_t st0 = item.n_other > 0 ? run_start(qr0) : 0;
+  const int64_t st1 = item.n_other > 1 ? run_start(qr1) : 0;
+  const int64_t nt0 = item.n_other > 0 ? (qr0.len - st0 + kRows - 1) / kRows : 0;
+  const int64_t nt1 = item.n_other > 1 ? (qr1.len - st1 + kRows - 1) / kRows : 0;
+  const int64_t per_head = nt0 + nt1;
   const int64_t T = per_head * p.group;
   struct QT {
     int64_t row0;  // flattened row index in [B * q_rows]
@@ -256,13 +261,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
     // 32-bit: a workgroup walks far fewer than 2^31 tiles
     const int32_t g = (int32_t)((uint32_t)t / (uint32_t)per_head);
     int64_t r = t - (int64_t)g * per_head;
-    const int ri = r < nt[0] ? 0 : 1;
-    if (ri) r -= nt[0];
-    const int64_t i0 = st[ri] + r * kRows;
-    const int64_t rem = qrun[ri].len - i0;
+    const bool second = r >= nt0;
+    if (second) r -= nt0;
+    const int64_t i0 = (second ? st1 : st0) + r * kRows;
+    const int64_t rem = (second ? qr1.len : qr0.len) - i0;
     x.rows = rem < kRows ? (int)rem : kRows;
-    x.row0 = (int64_t)b * p.q_rows + p.q_off + qrun[ri].row0 + i0;
-    x.pos0 = qrun[ri].pos0 + i0;
+    x.row0 = (int64_t)b * p.q_rows + p.q_off + (second ? qr1.row0 : qr0.row0) + i0;
+    x.pos0 = (second ? qr1.pos0 : qr0.pos0) + i0;
     x.hq = hkv * p.group + (int32_t)g;
     return x;
   };
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
   const BwdItem item = bwd_q_item(p, kOwn, tl);
   if (item.tile.rows <= 0) return;  // varlen: a tile past the end of its sequence
   const BwdTile qt = item.tile;
-  const BwdRun* krun = item.other;
+  const BwdRun kr0 = item.other[0], kr1 = item.other[1];  // scalars, as in the dK/dV kernel
   const int wq0 = 32 * wave;
   const int wqrows = qt.rows - wq0 < 0 ? 0 : (qt.rows - wq0 > 32 ? 32 : (int)(qt.rows - wq0));
   const bool q_valid = l32 < wqrows;
@@ -447,10 +452,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
 
   // key tiles: the live prefix of every key run
-  int64_t nt[2] = {0, 0};
-  for (int ri = 0; ri < item.n_other; ++ri)
-    nt[ri] = live_tiles(Run{krun[ri].row0, krun[ri].len, krun[ri].pos0}, qhi, p.causal, kRows);
-  const int64_t T = nt[0] + nt[1];
+  const int64_t nt0 =
+      item.n_other > 0 ? live_tiles(Run{kr0.row0, kr0.len, kr0.pos0}, qhi, p.causal, kRows) : 0;
+  const int64_t nt1 =
+      item.n_other > 1 ? live_tiles(Run{kr1.row0, kr1.len, kr1.pos0}, qhi, p.causal, kRows) : 0;
+  const int64_t T = nt0 + nt1;
   struct KT {
     int64_t row0;
     int64_t pos0;
@@ -458,12 +464,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
   };
   auto tile_of = [&](int64_t t) {
     KT x;
-    const int ri = t < nt[0] ? 0 : 1;
-    const int64_t tt = ri ? t - nt[0] : t;
-    const int64_t rem = krun[ri].len - tt * kRows;
+    const bool second = t >= nt0;
+    const int64_t tt = second ? t - nt0 : t;
+    const int64_t rem = (second ? kr1.len : kr0.len) - tt * kRows;
     x.rows = rem < kRows ? (int)rem : kRows;
-    x.row0 = (int64_t)b * p.k_rows + p.k_off + krun[ri].row0 + tt * kRows;
-    x.pos0 = krun[ri].pos0 + tt * kRows;
+    x.row0 = (int64_t)b * p.k_rows + p.k_off + (second ? kr1.row0 : kr0.row0) + tt * kRows;
+    x.pos0 = (second ? kr1.pos0 : kr0.pos0) + tt * kRows;
     return x;
   };
   const int64_t kstride = (int64_t)p.Hkv * D;
