@@ -35,7 +35,11 @@ _lib = None
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
-    """Load librattn.so (built by ring_attention_amd.build) and declare signatures."""
+    """Load librattn.so and declare signatures.
+
+    With no path: the in-tree build (ring_attention_amd.build), loaded once.
+    With a path: that build of the library, which the wrappers below call from
+    then on."""
     global _lib
     if _lib is not None and path is None:
         return _lib
@@ -79,8 +83,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                               i32, f32, i32, i64p, i64p, i64p, i64p, vp]
     lib.rattn_status_string.restype = ctypes.c_char_p
     lib.rattn_status_string.argtypes = [i32]
-    if path is None:
-        _lib = lib
+    _lib = lib
     return lib
 
 
