@@ -453,6 +453,17 @@ def main():
                                  "ms": round(sep_ms, 4), "merge_avg_ms": round(merge_ms, 4)},
         "fused": {"value": round(fused_value, 2), "ms": round(fused_ms, 4),
                   "pct_of_peak": round(100 * fused_value / PEAK_BF16_TFLOPS, 2)},
+        # context only, not a target: the memory-wall figures of the
+        # guijiagi.com ring-attention page (naive attention section) -- a full
+        # fp16 score matrix at one million tokens against one GPU's HBM
+        "page_context": {
+            "score_matrix_1M_tokens_fp16_bytes": 10**6 * 10**6 * 2,
+            "page_gpu_hbm_bytes": 80 * 10**9,
+            "page_gpu": "unnamed 80 GB GPU",
+            "this_gpu_hbm_bytes": 288 * 10**9,
+            "score_matrix_bytes_this_workload_if_materialised":
+                2 * w.B * Hq * w.Nq * N,
+            "score_bytes_materialised_here": 0},
     }
     del fo, fl
 
