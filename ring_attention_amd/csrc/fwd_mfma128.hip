@@ -11,12 +11,13 @@
 // waves w and w+4 share a SIMD.  Waves 0-3 form group A, waves 4-7 group B.
 // Per key tile k each group runs an MFMA phase M_k = {PV of tile k-1, QK of
 // tile k} (32 MFMAs) and a VALU phase V_k = {mask, max, exp, sum, P} of tile
-// k.  Group B runs one phase behind group A and a workgroup barrier ends
-// every phase ("slot"), so in each slot one group's softmax runs next to the
-// other group's matrix work on every SIMD:
-//      slot   0    1    2    3    4   ...
-//      A     M0   V0   M1   V1   M2
-//      B     --   M0   V0   M1   V1
+// k.  Group B runs one phase behind group A, so one group's softmax runs
+// next to the other group's matrix work on every SIMD:
+//      window   0  |  1  |   2    |   3    |  ...
+//      A        M0 | V0  | M1  V1 | M2  V2 |
+//      B        -- | M0  | V0  M1 | V1  M2 |
+// A workgroup barrier ends every window (A's after its V phase, B's after
+// its M phase), one per key tile; inside a window the groups run unsynchronised.
 //
 // Every M phase runs the same 32-MFMA stream (a single code path keeps the
 // accumulators in place); a tile a wave does not score gets P = 0.  The
@@ -25,8 +26,8 @@
 // opens by issuing this wave's share of the DMA of a later tile.
 //
 // Data path.  K and V tiles (64 keys x 128 dims) move global -> LDS by
-// direct-to-LDS DMA into a ring of 4 buffers; tile k is requested three or
-// four slots before group A's QK reads it.  Rows
+// direct-to-LDS DMA into a ring of 4 buffers; tile k is requested two
+// windows before group A's QK reads it.  Rows
 // are stored with XOR-swizzled 16-byte chunks (K chunk c of row r at slot
 // c ^ (r%16), V at c ^ 4(r%4)) so the fragment reads below are conflict-free.
 // S^T = K Q^T with v_mfma_f32_32x32x16 (A = K fragment, B = Q held in
@@ -370,41 +371,39 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
     l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
 
-  // Before group A's QK of tile j (even slot 2j) tile j must have landed on
-  // every wave; only tile j+1's requests may still be in flight.
+  // Before the window in which the groups score tile j, tile j must have
+  // landed on every wave; only tile j+1's requests may still be in flight.
   auto wait_tile = [&](int j) {
     if (j + 1 < T) wait_dma_but_one_tile(); else wait_dma_all();
   };
 
-  // DMA: each wave requests its share of tile m at the start of its M phase
-  // for tile m-2, group A in slot 2m-4, group B in slot 2m-3.  Buffer m%4
-  // last held tile m-4, whose last reader (group B's PV) ran in slot 2m-5.
-  // Every wave waits for tile m at the end of slot 2m-1, before group A's QK
-  // reads it; only tile m+1's requests may still be in flight then.  The
-  // DMA issue (scalar and memory instructions) fits between the MFMAs.
-  // Both groups pass 2T+2 barriers.
+  // Windows.  Window 0 is group A's M0, window 1 A's V0 and B's M0; window
+  // k >= 2 holds A's M_{k-1}, V_{k-1} and B's V_{k-2}, M_{k-1}.  Window k ends
+  // with the barrier both groups pass after waiting for their part of tile k.
+  // Each wave requests its share of tile m at the start of its M phase for
+  // tile m-2, in window m-1 (group A's request of tile 2: window 0).  Buffer
+  // m%4 last held tile m-4, whose last readers (the PV in both groups'
+  // M_{m-3}, window m-2) finished at the barrier ending window m-2.  Tile m
+  // is complete on every wave at the barrier ending window m, before any QK
+  // of tile m (window m+1).  Both groups pass T+1 barriers.
   if (group == 0) {
+    m_phase(0);
+    slot_barrier();
     for (int j = 0; j < T; ++j) {
-      m_phase(j);      // slot 2j (requests tile j+2)
-      slot_barrier();
-      v_phase();       // slot 2j+1
+      v_phase();
       wait_tile(j + 1);
       slot_barrier();
+      m_phase(j + 1);  // requests tile j+3; for j+1 = T: PV of the last tile
     }
-    m_phase(T);        // slot 2T: PV of the last tile
-    slot_barrier();
-    slot_barrier();    // slot 2T+1
   } else {
-    slot_barrier();    // slot 0
+    slot_barrier();
     for (int j = 0; j < T; ++j) {
-      m_phase(j);      // slot 2j+1 (requests tile j+2)
+      m_phase(j);      // requests tile j+2
       wait_tile(j + 1);
       slot_barrier();
-      v_phase();       // slot 2j+2
-      slot_barrier();
+      v_phase();
     }
-    m_phase(T);        // slot 2T+1
-    slot_barrier();
+    m_phase(T);        // PV of the last tile
   }
   // ---- epilogue: O / l, LSE = m ln2 + ln l --------------------------------
   const float l_tot = pair_sum(l_run);
