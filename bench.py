@@ -276,6 +276,34 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in self.pairs)
 
 
+def warm_up(torch, fn, calls, min_s=0.25):
+    """Untimed calls before an extra's timing: at least `calls`, and at least
+    `min_s` seconds of them, so that a short workload is timed at the clock
+    the GPU reaches under load (after a pause it starts lower and ramps up)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < calls or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def loop_ms(torch, fn, reps):
+    """Average milliseconds per call of `reps` back-to-back calls, timed by one
+    pair of HIP events on the current stream.  Per-call event pairs would also
+    count the host's launch overhead whenever the GPU waits for the next call,
+    which inflates calls of a few hundred microseconds."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def step_plan(N, W, rank, c):
     """The launches of one ZigZag ring device (as ring.ring_forward_steps runs
     them): per step the query runs, key runs and whether it is merged."""
@@ -403,10 +431,7 @@ def main():
     # float32 partials, rattn_merge folds them in)
     for _ in range(args.warmup):
         one_step(fused_merge=False)
-    sep = Timer(torch)
-    for _ in range(args.steps):
-        sep(lambda: one_step(fused_merge=False))
-    sep_ms = sep.total_ms() / args.steps
+    sep_ms = loop_ms(torch, lambda: one_step(fused_merge=False), args.steps)
     for _ in range(args.steps):
         one_step(hook, fused_merge=False)
     merge_ms = merge_t.total_ms() / max(1, len(merge_t.pairs))
@@ -415,10 +440,8 @@ def main():
     fo = fl = None
     for _ in range(args.warmup):
         fo, fl = binding.fwd(q, k, v, causal=True, n_ring_steps=W, zigzag=True, rank=rank)
-    ft = Timer(torch)
-    for _ in range(args.steps):
-        ft(lambda: binding.fwd(q, k, v, causal=True, n_ring_steps=W, zigzag=True, rank=rank))
-    fused_ms = ft.total_ms() / args.steps
+    fused_ms = loop_ms(torch, lambda: binding.fwd(q, k, v, causal=True, n_ring_steps=W,
+                                                  zigzag=True, rank=rank), args.steps)
     fused_value = flop_per_step / (fused_ms * 1e-3) / 1e12
 
     result = {
@@ -480,14 +503,12 @@ def main():
                 pe = we.Nq * we.N
             fe = 4 * we.d * we.Hq * we.B * pe
             reps = 3 if idx == 5 else args.steps
-            for _ in range(1 if idx == 5 else args.warmup):
-                binding.fwd(qe, ke, ve, causal=we.causal, n_ring_steps=we.W, zigzag=we.zigzag,
-                            rank=we.rank)
-            te = Timer(torch)
-            for _ in range(reps):
-                te(lambda: binding.fwd(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
-                                       zigzag=we.zigzag, rank=we.rank))
-            ms = te.total_ms() / reps
+            warm_up(torch, lambda: binding.fwd(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
+                                               zigzag=we.zigzag, rank=we.rank),
+                    1 if idx == 5 else args.warmup, 0.0 if idx == 5 else 0.25)
+            ms = loop_ms(torch, lambda: binding.fwd(qe, ke, ve, causal=we.causal,
+                                                    n_ring_steps=we.W, zigzag=we.zigzag,
+                                                    rank=we.rank), reps)
             extras[we.name] = {"ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
                                "pct_of_peak": round(100 * fe / (ms * 1e-3) / 1e12
                                                     / PEAK_BF16_TFLOPS, 2)}
@@ -499,12 +520,8 @@ def main():
                 def run_split():
                     return binding.fwd_split(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
                                              zigzag=we.zigzag, rank=we.rank, n_splits=ns, ws=ws)
-                for _ in range(args.warmup):
-                    run_split()
-                te = Timer(torch)
-                for _ in range(reps):
-                    te(run_split)
-                ms = te.total_ms() / reps
+                warm_up(torch, run_split, args.warmup)
+                ms = loop_ms(torch, run_split, reps)
                 extras[we.name + "_splitkv"] = {
                     "ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
                     "pct_of_peak": round(100 * fe / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
@@ -556,12 +573,8 @@ def backward_extras(torch, binding, ring, workloads, dev, args):
             return binding.bwd(q, k, v, out, lse, do, causal=w.causal, n_ring_steps=w.W,
                                zigzag=w.zigzag, rank=w.rank, dq=dq, dk=dk, dv=dv, delta_ws=ws)
         reps = max(3, args.steps // 2)
-        for _ in range(max(1, args.warmup)):
-            run()
-        te = Timer(torch)
-        for _ in range(reps):
-            te(run)
-        ms = te.total_ms() / reps
+        warm_up(torch, run, max(1, args.warmup))
+        ms = loop_ms(torch, run, reps)
         tf = flop / (ms * 1e-3) / 1e12
         res[w.name + "_bwd"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
                                 "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
@@ -573,12 +586,8 @@ def backward_extras(torch, binding, ring, workloads, dev, args):
             def run_steps():
                 return ring.ring_backward_steps(q, ks, vs, out, lse, do, w.W, True, w.rank,
                                                 causal=True)
-            for _ in range(max(1, args.warmup)):
-                run_steps()
-            te = Timer(torch)
-            for _ in range(reps):
-                te(run_steps)
-            ms = te.total_ms() / reps
+            warm_up(torch, run_steps, max(1, args.warmup))
+            ms = loop_ms(torch, run_steps, reps)
             tf = flop / (ms * 1e-3) / 1e12
             res[w.name + "_bwd_ring_steps"] = {
                 "ms": round(ms, 4), "tflops": round(tf, 2),
@@ -646,14 +655,10 @@ def layout_comparison(torch, binding, ring, workloads, dev, args):
                 for s in range(W):
                     src = (r - s) % W
                     steps.append((qp, runs_positions(ring.shard_rows(N, W, zz, src))))
-        for r in range(W):  # warm every device's share first
-            run(r)
+        warm_up(torch, lambda: [run(r) for r in range(W)], 1)  # every device's share
         ms = []
         for r in range(W):
-            te = Timer(torch)
-            for _ in range(3):
-                te(lambda: run(r))
-            ms.append(te.total_ms() / 3)
+            ms.append(loop_ms(torch, lambda: run(r), 3))
         ring_ms = max(ms)
         res["layout_" + layout] = {
             "device_ms": [round(x, 3) for x in ms], "ring_step_ms": round(ring_ms, 3),
@@ -678,13 +683,9 @@ def varlen_extra(torch, binding, workloads, dev, args):
 
     def run():
         return binding.fwd_varlen(q, k, v, starts, ls, starts, ls, causal=True)
-    for _ in range(max(1, args.warmup)):
-        run()
-    te = Timer(torch)
+    warm_up(torch, run, max(1, args.warmup))
     reps = max(3, args.steps // 2)
-    for _ in range(reps):
-        te(run)
-    ms = te.total_ms() / reps
+    ms = loop_ms(torch, run, reps)
     tf = flop / (ms * 1e-3) / 1e12
     del q, k, v
     torch.cuda.empty_cache()
@@ -705,12 +706,8 @@ def small_d_sweep(torch, binding, workloads, dev, args):
                                         seed=3, device=dev)
         fe = 4 * dd * w3.Hq * w3.B * pe
         comp = (qe.numel() + ke.numel() + ve.numel() + qe.numel()) * 2 + qe.numel() // dd * 4
-        for _ in range(args.warmup):
-            binding.fwd(qe, ke, ve, causal=True)
-        te = Timer(torch)
-        for _ in range(args.steps):
-            te(lambda: binding.fwd(qe, ke, ve, causal=True))
-        ms = te.total_ms() / args.steps
+        warm_up(torch, lambda: binding.fwd(qe, ke, ve, causal=True), args.warmup)
+        ms = loop_ms(torch, lambda: binding.fwd(qe, ke, ve, causal=True), args.steps)
         out[f"mha_causal_b2_h32_4k_d{dd}_f16"] = {
             "ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
             "compulsory_bytes": comp, "compulsory_GBps": round(comp / (ms * 1e-3) / 1e9, 1)}
