@@ -38,7 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
-STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, true>"  # d=128 16-bit path, fp32 partials
+STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, true, true>"  # d=128 16-bit path, fp32 partials
 # sources the step kernel is built from; the stored counter summary is valid
 # only for the kernel it was measured on
 KERNEL_SOURCES = ("fwd_mfma128.hip", "kcommon.h", "ring_sched.h", "launch.h")

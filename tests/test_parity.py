@@ -185,6 +185,37 @@ def test_workload5_long_context_gqa(gpu):
     compare(host(o), host(l), ref_o, ref_l, torch.bfloat16, what=w.name)
 
 
+def test_kv_rows_over_4gb(gpu):
+    # One key/value head's rows span more than 4 GB (1,048,640 rows of
+    # 16 heads x 128 x 2 bytes): past the range of the d = 128 kernel's
+    # buffer-offset DMA, so its 64-bit-address DMA runs.  Non-causal, every
+    # query sees all 1M keys; checked on sampled (row, head) pairs.
+    Nq, Nk, H, d = 256, 1_048_640, 16, 128
+    note("case kv rows over 4 GB: generating inputs on the GPU")
+    q, k, v = workloads.make_qkv(1, Nq, Nk, H, H, d, torch.bfloat16, seed=21, device=gpu)
+    assert Nk * H * d * 2 > 0xFFFF0000
+    # one ring step: 256 query rows against all key rows (float32 partial)
+    out, lse = binding.fwd_step(q, k, v, False, [(0, Nq)], [(0, Nk)])
+    torch.cuda.synchronize()
+    rows = np.array([(0, 0, 0), (0, 255, 15), (0, 100, 7), (0, 31, 8), (0, 32, 3)])
+    ridx = torch.as_tensor(rows, device=gpu)
+    o = out[ridx[:, 0], ridx[:, 1], ridx[:, 2]].cpu()
+    l = lse[ridx[:, 0], ridx[:, 1], ridx[:, 2]].cpu()
+    q_sel = q[ridx[:, 0], ridx[:, 1], ridx[:, 2]].cpu()
+    del out, lse, q
+    ref_o = np.zeros((len(rows), d))
+    ref_l = np.zeros(len(rows))
+    for i, (_, _, h) in enumerate(rows):
+        kh = k[:, :, h:h + 1].cpu().contiguous()
+        vh = v[:, :, h:h + 1].cpu().contiguous()
+        ro, rl = oracle.attention(q_sel[i].reshape(1, 1, 1, d).contiguous(), kh, vh,
+                                  causal=False)
+        ref_o[i] = ro[0, 0, 0]
+        ref_l[i] = rl[0, 0, 0]
+    compare(o.numpy().astype(np.float64), l.numpy().astype(np.float64), ref_o, ref_l,
+            torch.bfloat16, what="kv rows over 4 GB")
+
+
 # --------------------------------------------------------------------------
 # edge cases and variants at sizes the oracle checks in full
 
