@@ -63,6 +63,25 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
                : "v"(gptr), "s"(lds_addr)
                : "memory");
 }
+// Buffer form of dma16: 16 bytes per lane from a raw buffer resource plus a
+// 32-bit lane offset (buffer_load_dwordx4 ... lds); used while every input
+// tensor is below 4 GB.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i tensor_rsrc(const void* base) {
+  const uint64_t a = (uint64_t)base;
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
+  r[2] = -1;           // num_records 2^32 - 1
+  r[3] = 0x00020000;   // 32-bit data format
+  return r;
+}
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // chunk-slot swizzle of row r (see the file comment)
@@ -125,16 +144,23 @@ __device__ __forceinline__ typename TT::v8 tr_frag(const char* tile, const FragO
 // the flattened row space (stride `stride` elements between rows); rows past
 // `rows` repeat the last one (finite, masked by the caller).  This wave moves
 // rows 16 w .. 16 w + 15, four 1 KB blocks.
-template <typename E>
-__device__ __forceinline__ void dma_tile(const E* base, int64_t row0, int rows, int64_t stride,
-                                         uint32_t lds_tile, int wave, int lane) {
+// `tensor` + `col0` elements is the tile's first column (BUF: `rsrc` is the
+// tensor as a buffer resource and the lane offsets are 32-bit).
+template <bool BUF, typename E>
+__device__ __forceinline__ void dma_tile(const E* tensor, v4i rsrc, int64_t col0, int64_t row0,
+                                         int rows, int64_t stride, uint32_t lds_tile, int wave,
+                                         int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * wave + 4 * i + (lane >> 4);
     const int rc = r < rows ? r : rows - 1;
-    const char* src = (const char*)(base + (row0 + rc) * stride) +
-                      16 * ((lane & 15) ^ swz(r));
-    dma16(src, lds_tile + (uint32_t)((16 * wave + 4 * i) * kRowBytes));
+    const int64_t e = (row0 + rc) * stride + col0;
+    const uint32_t chunk = 16 * ((lane & 15) ^ swz(r));
+    const uint32_t dst = lds_tile + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
+    if (BUF)
+      dma16(rsrc, (uint32_t)(e * (int64_t)sizeof(E)) + chunk, dst);
+    else
+      dma16((const char*)(tensor + e) + chunk, dst);
   }
 }
 
@@ -179,7 +205,7 @@ __device__ __forceinline__ void work_order(int32_t BH, int64_t n_tiles, bool hea
 }
 
 // ---- dK, dV ------------------------------------------------------------------
-template <typename TT, bool ACC>
+template <typename TT, bool ACC, bool BUF>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, const typename TT::elem* __restrict__ dout,
@@ -272,11 +298,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
     return x;
   };
   const int64_t qstride = (int64_t)p.Hq * D;
+  const v4i qrs = BUF ? tensor_rsrc(q) : v4i{}, grs = BUF ? tensor_rsrc(dout) : v4i{};
   auto issue = [&](int64_t t, int buf) {
     const QT x = tile_of(t);
     const uint32_t base = smem_addr + buf * kBufBytes;
-    dma_tile(q + (int64_t)x.hq * D, x.row0, x.rows, qstride, base, wave, lane);
-    dma_tile(dout + (int64_t)x.hq * D, x.row0, x.rows, qstride, base + kTileBytes, wave, lane);
+    dma_tile<BUF>(q, qrs, (int64_t)x.hq * D, x.row0, x.rows, qstride, base, wave, lane);
+    dma_tile<BUF>(dout, grs, (int64_t)x.hq * D, x.row0, x.rows, qstride, base + kTileBytes, wave,
+                  lane);
     if (wave < 2) {
       const int rc = lane < x.rows ? lane : x.rows - 1;
       const float* src = (wave == 0 ? lse : delta) + (x.row0 + rc) * p.Hq + x.hq;
@@ -397,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
 }
 
 // ---- dQ ----------------------------------------------------------------------
-template <typename TT, bool ACC>
+template <typename TT, bool ACC, bool BUF>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, const typename TT::elem* __restrict__ dout,
@@ -473,11 +501,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
     return x;
   };
   const int64_t kstride = (int64_t)p.Hkv * D;
+  const v4i krs = BUF ? tensor_rsrc(k) : v4i{}, vrs = BUF ? tensor_rsrc(v) : v4i{};
   auto issue = [&](int64_t t, int buf) {
     const KT x = tile_of(t);
     const uint32_t base = smem_addr + buf * kBufBytes;
-    dma_tile(k + (int64_t)hkv * D, x.row0, x.rows, kstride, base, wave, lane);
-    dma_tile(v + (int64_t)hkv * D, x.row0, x.rows, kstride, base + kTileBytes, wave, lane);
+    dma_tile<BUF>(k, krs, (int64_t)hkv * D, x.row0, x.rows, kstride, base, wave, lane);
+    dma_tile<BUF>(v, vrs, (int64_t)hkv * D, x.row0, x.rows, kstride, base + kTileBytes, wave,
+                  lane);
   };
 
   const FragOff fo = frag_offsets(lane);
@@ -570,19 +600,33 @@ hipError_t launch_acc(const void* q, const void* k, const void* v, const void* d
                       const float* lse, const float* delta, void* dq, void* dk, void* dv,
                       const BwdParams& p, hipStream_t stream) {
   using E = typename TT::elem;
+  // buffer-form DMA while q, dO, k and v are each below 4 GB (32-bit offsets)
+  const uint64_t lim = 0xFFFF0000ull;
+  const bool buf = (uint64_t)p.B * p.q_rows * p.Hq * D * sizeof(E) <= lim &&
+                   (uint64_t)p.B * p.k_rows * p.Hkv * D * sizeof(E) <= lim;
   const int64_t qb = bwd_q_tiles(p, kOwn) * p.B * p.Hq;
   if (qb > 0) {
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<TT, ACC>), dim3((unsigned)qb), dim3(kThreads), 0,
-                       stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,
-                       dq, p);
+    if (buf)
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<TT, ACC, true>), dim3((unsigned)qb), dim3(kThreads),
+                         0, stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse,
+                         delta, dq, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_mfma_kernel<TT, ACC, false>), dim3((unsigned)qb),
+                         dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                         (const E*)dout, lse, delta, dq, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t kb = bwd_k_tiles(p, kOwn) * p.B * p.Hkv;
   if (kb > 0) {
-    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<TT, ACC>), dim3((unsigned)kb), dim3(kThreads), 0,
-                       stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse, delta,
-                       dk, dv, p);
+    if (buf)
+      hipLaunchKernelGGL((bwd_dkv_mfma_kernel<TT, ACC, true>), dim3((unsigned)kb),
+                         dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                         (const E*)dout, lse, delta, dk, dv, p);
+    else
+      hipLaunchKernelGGL((bwd_dkv_mfma_kernel<TT, ACC, false>), dim3((unsigned)kb),
+                         dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                         (const E*)dout, lse, delta, dk, dv, p);
     return hipGetLastError();
   }
   return hipSuccess;
