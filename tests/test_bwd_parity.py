@@ -324,3 +324,44 @@ def test_bwd_workload4_sampled(gpu):
             w.name, rel=5e-2)
     compare("dv (ring steps)", np.transpose(gv, (1, 0, 2)).reshape(-1, w.d), rv, q.dtype,
             w.name, rel=5e-2)
+
+
+def test_bwd_kv_rows_over_4gb(gpu):
+    """One backward ring step whose key/value tensors exceed 4 GB (1,048,640
+    rows x 16 heads x 128 x 2 bytes): both backward kernels take their
+    64-bit-address DMA path.  Non-causal: every query sees all 1M keys, so the
+    gradients are tiny and the bar is relative (as for the ring share).  dQ on
+    sampled query rows; dK, dV on three key rows of one head."""
+    Nq, Nk, H, d = 256, 1_048_640, 16, 128
+    dev = torch.device("cuda:0")
+    note("case bwd kv rows over 4 GB: generating inputs on the GPU")
+    q, k, v = workloads.make_qkv(1, Nq, Nk, H, H, d, torch.bfloat16, seed=22, device=dev)
+    assert Nk * H * d * 2 > 0xFFFF0000
+    g = torch.Generator(device=dev).manual_seed(23)
+    do = workloads.randn(q.shape, q.dtype, g, dev)
+    out, lse = binding.fwd_step(q, k, v, False, [(0, Nq)], [(0, Nk)])  # all keys: final out
+    delta = (out * do.float()).sum(-1).contiguous()                    # D = rowsum(dO o O)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=dev)
+    binding.bwd_step(q, k, v, do, lse, delta, dq, dk, dv, False, [(0, Nq)], [(0, Nk)])
+    torch.cuda.synchronize()
+    head = 4
+    krows = np.array([[0, 0, head], [0, Nk - 1, head], [0, 524_288, head]])
+    kidx = torch.as_tensor(krows, device=dev)
+    gk = dk[kidx[:, 0], kidx[:, 1], kidx[:, 2]].cpu().numpy().astype(np.float64)
+    gv = dv[kidx[:, 0], kidx[:, 1], kidx[:, 2]].cpu().numpy().astype(np.float64)
+    del dk, dv, out, lse, delta
+    qc, kc, vc, doc = (t.cpu() for t in (q, k, v, do))
+    qrows = np.array([[0, 0, 0], [0, Nq - 1, H - 1], [0, 77, 9]])
+    allrows = np.concatenate([qrows, [[0, i, head] for i in range(Nq)]])
+    lse_all = np.full((1, Nq, H), np.nan)
+    dl_all = np.full((1, Nq, H), np.nan)
+    lr, dr = oracle.bwd_stats(qc, kc, vc, doc, causal=False, rows=allrows)
+    lse_all[0, allrows[:, 1], allrows[:, 2]] = lr
+    dl_all[0, allrows[:, 1], allrows[:, 2]] = dr
+    rq = oracle.bwd_dq(qc, kc, vc, doc, lse_all, dl_all, causal=False, rows=qrows)
+    compare("dq", host(dq)[0, qrows[:, 1], qrows[:, 2]], rq, q.dtype, "kv over 4 GB", rel=5e-2)
+    rk, rv = oracle.bwd_dkv(qc, kc, vc, doc, lse_all, dl_all, causal=False, rows=krows)
+    compare("dk", gk, rk, q.dtype, "kv over 4 GB", rel=5e-2)
+    compare("dv", gv, rv, q.dtype, "kv over 4 GB", rel=5e-2)
