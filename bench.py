@@ -208,7 +208,7 @@ def summarize_kernels(fetch_csv: str, write_csv: str, sq_csv: str) -> None:
             float(r["Counter_Value"])
         dur.setdefault(name, {})[r["Dispatch_Id"]] = \
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-    print(f"{'kernel':46s} {'n':>4s} {'avg_us':>9s} {'HBM_MB':>8s} {'GB/s':>8s} "
+    print(f"{'kernel':58s} {'n':>4s} {'avg_us':>9s} {'HBM_MB':>8s} {'GB/s':>8s} "
           f"{'mfma_busy':>9s} {'valu_instr/disp':>15s}")
     for name in sorted(per):
         d = per[name]
@@ -220,7 +220,7 @@ def summarize_kernels(fetch_csv: str, write_csv: str, sq_csv: str) -> None:
         if name in fetch and name in write:
             hbm = (sum(fetch[name]) / len(fetch[name]) * f_scale +
                    sum(write[name]) / len(write[name]) * w_scale) * 1024
-        print(f"{name[:46]:46s} {n:4d} {t * 1e6:9.1f} "
+        print(f"{name[:58]:58s} {n:4d} {t * 1e6:9.1f} "
               f"{(hbm or 0) / 1e6:8.1f} {(hbm or 0) / t / 1e9:8.1f} "
               f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:9.4f} {avg['SQ_INSTS_VALU']:15.4g}")
 
