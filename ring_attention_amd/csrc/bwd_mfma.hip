@@ -76,10 +76,12 @@ __device__ __forceinline__ v4i tensor_rsrc(const void* base) {
   r[3] = 0x00020000;   // 32-bit data format
   return r;
 }
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+// soff: the wave-uniform part of the offset (scalar), voff: the lane part
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t soff, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -154,13 +156,13 @@ __device__ __forceinline__ void dma_tile(const E* tensor, v4i rsrc, int64_t col0
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * wave + 4 * i + (lane >> 4);
     const int rc = r < rows ? r : rows - 1;
-    const int64_t e = (row0 + rc) * stride + col0;
     const uint32_t chunk = 16 * ((lane & 15) ^ swz(r));
     const uint32_t dst = lds_tile + (uint32_t)((16 * wave + 4 * i) * kRowBytes);
     if (BUF)
-      dma16(rsrc, (uint32_t)(e * (int64_t)sizeof(E)) + chunk, dst);
+      dma16(rsrc, (uint32_t)((row0 * stride + col0) * (int64_t)sizeof(E)),
+            (uint32_t)(rc * stride * (int64_t)sizeof(E)) + chunk, dst);
     else
-      dma16((const char*)(tensor + e) + chunk, dst);
+      dma16((const char*)(tensor + (row0 + rc) * stride + col0) + chunk, dst);
   }
 }
 
