@@ -326,17 +326,23 @@ def test_bwd_workload4_sampled(gpu):
             w.name, rel=5e-2)
 
 
-def test_bwd_kv_rows_over_4gb(gpu):
-    """One backward ring step whose key/value tensors exceed 4 GB (1,048,640
-    rows x 16 heads x 128 x 2 bytes): both backward kernels take their
-    64-bit-address DMA path.  Non-causal: every query sees all 1M keys, so the
-    gradients are tiny and the bar is relative (as for the ring share).  dQ on
-    sampled query rows; dK, dV on three key rows of one head."""
-    Nq, Nk, H, d = 256, 1_048_640, 16, 128
+@pytest.mark.parametrize("Nk", [1_048_560, 1_048_600],
+                         ids=["buffer_offsets_at_limit", "over_4gb_64bit_addresses"])
+def test_bwd_kv_rows_at_and_over_4gb(gpu, Nk):
+    """One backward ring step whose key/value tensors (Nk rows x 16 heads x
+    128 x 2 bytes) fill 0xFFFF0000 bytes exactly -- the largest the backward
+    kernels still read through 32-bit buffer offsets -- or exceed 4 GB, where
+    they take their 64-bit-address DMA.  Both end in a ragged key tile.
+    Non-causal: every query sees all 1M keys, so the gradients are tiny and
+    the bar is relative (as for the ring share).  dQ on sampled query rows;
+    dK, dV on key rows of one head at the first and last row, byte offset
+    2**31, the first row of the last 64-row tile and (over 4 GB) byte offset
+    2**32."""
+    Nq, H, d = 256, 16, 128
     dev = torch.device("cuda:0")
-    note("case bwd kv rows over 4 GB: generating inputs on the GPU")
+    note(f"case bwd kv rows Nk={Nk}: generating inputs on the GPU")
     q, k, v = workloads.make_qkv(1, Nq, Nk, H, H, d, torch.bfloat16, seed=22, device=dev)
-    assert Nk * H * d * 2 > 0xFFFF0000
+    assert (Nk * H * d * 2 <= 0xFFFF0000) == (Nk == 1_048_560)
     g = torch.Generator(device=dev).manual_seed(23)
     do = workloads.randn(q.shape, q.dtype, g, dev)
     out, lse = binding.fwd_step(q, k, v, False, [(0, Nq)], [(0, Nk)])  # all keys: final out
@@ -347,7 +353,8 @@ def test_bwd_kv_rows_over_4gb(gpu):
     binding.bwd_step(q, k, v, do, lse, delta, dq, dk, dv, False, [(0, Nq)], [(0, Nk)])
     torch.cuda.synchronize()
     head = 4
-    krows = np.array([[0, 0, head], [0, Nk - 1, head], [0, 524_288, head]])
+    krows = np.array([[0, 0, head], [0, Nk - 1, head], [0, 524_288, head],
+                      [0, Nk - Nk % 64, head], [0, min(1_048_576, Nk - 30), head]])
     kidx = torch.as_tensor(krows, device=dev)
     gk = dk[kidx[:, 0], kidx[:, 1], kidx[:, 2]].cpu().numpy().astype(np.float64)
     gv = dv[kidx[:, 0], kidx[:, 1], kidx[:, 2]].cpu().numpy().astype(np.float64)
@@ -361,7 +368,8 @@ def test_bwd_kv_rows_over_4gb(gpu):
     lse_all[0, allrows[:, 1], allrows[:, 2]] = lr
     dl_all[0, allrows[:, 1], allrows[:, 2]] = dr
     rq = oracle.bwd_dq(qc, kc, vc, doc, lse_all, dl_all, causal=False, rows=qrows)
-    compare("dq", host(dq)[0, qrows[:, 1], qrows[:, 2]], rq, q.dtype, "kv over 4 GB", rel=5e-2)
+    compare("dq", host(dq)[0, qrows[:, 1], qrows[:, 2]], rq, q.dtype, f"kv rows Nk={Nk}",
+            rel=5e-2)
     rk, rv = oracle.bwd_dkv(qc, kc, vc, doc, lse_all, dl_all, causal=False, rows=krows)
-    compare("dk", gk, rk, q.dtype, "kv over 4 GB", rel=5e-2)
-    compare("dv", gv, rv, q.dtype, "kv over 4 GB", rel=5e-2)
+    compare("dk", gk, rk, q.dtype, f"kv rows Nk={Nk}", rel=5e-2)
+    compare("dv", gv, rv, q.dtype, f"kv rows Nk={Nk}", rel=5e-2)
