@@ -24,17 +24,53 @@ def _exp_shift(x, m):
     return np.where(np.isneginf(x), 0.0, r)
 
 
-def blockwise_attention(q, k, v, Br: int, Bc: int, scale: float | None = None,
-                        causal: bool = False, q_pos=None, k_pos=None):
-    """Online-softmax attention over query tiles of Br rows and key tiles of Bc
-    rows, with the division by l deferred to the end.
+def _stream_tiles(q, tiles, scale: float):
+    """Online softmax of the rows of q over a sequence of key/value tiles.
 
-    Follows the FlashAttention forward recurrence of the yz520gzy chapter
-    (tile counts ceil(N/B), so ragged tails are kept) with the FlashAttention-2
-    change described there (keep O unnormalised, divide once), and the
-    youngju.dev ``blockwise_attention`` update (m_new = max(m, rowmax S),
-    correction exp(m - m_new)).  Causal masking by position: a key later than
-    the query gets score -inf (the youngju.dev causal step).
+    State per query row: the running maximum m of the scaled scores and an
+    accumulator A = [O | l] over the value columns augmented with a column of
+    ones, since the denominator l is the same exponential-weighted sum as O
+    with every value replaced by 1.  A tile with scores S (masked entries
+    -inf) moves the state to m' = max(m, max_j S_j) and
+    A' = exp(m - m') A + exp(S - m') [V | 1]; after the last tile
+    O = A[:, :d] / A[:, d] and lse = m' + log A[:, d] (rows that saw no key
+    keep O = 0, lse = -inf).  tiles: (K_t, V_t, hidden_t) with hidden_t a
+    boolean [rows, keys] mask or None.
+    """
+    n, dv = q.shape[0], None
+    m = np.full(n, -np.inf)
+    acc = None
+    for kt, vt, hidden in tiles:
+        s_t = (q @ kt.T) * scale
+        if hidden is not None:
+            s_t = np.where(hidden, -np.inf, s_t)
+        v_aug = np.concatenate([vt, np.ones((vt.shape[0], 1))], axis=1)
+        if acc is None:
+            dv = vt.shape[1]
+            acc = np.zeros((n, dv + 1))
+        m_next = np.maximum(m, s_t.max(axis=1, initial=-np.inf))
+        acc = _exp_shift(m, m_next)[:, None] * acc + _exp_shift(s_t, m_next[:, None]) @ v_aug
+        m = m_next
+    den = acc[:, dv]
+    out = np.zeros((n, dv))
+    lse = np.full(n, -np.inf)
+    seen = den > 0
+    out[seen] = acc[seen, :dv] / den[seen, None]
+    lse[seen] = m[seen] + np.log(den[seen])
+    return out, lse
+
+
+def tiled_online_softmax(q, k, v, Br: int, Bc: int, scale: float | None = None,
+                         causal: bool = False, q_pos=None, k_pos=None):
+    """Attention computed tile by tile: query tiles of Br rows, each streaming
+    key/value tiles of Bc rows through the online softmax (``_stream_tiles``),
+    one division at the end.
+
+    The recurrence is the FlashAttention forward of the yz520gzy chapter
+    (ceil(N / B) tiles per side, so ragged tails are kept; the
+    FlashAttention-2 variant's single normalisation) with the running-max
+    correction of the youngju.dev blockwise attention; causal masking by
+    position (a key after the query is hidden).
     Returns (O [Nq, d], lse [Nq]).
     """
     q = np.asarray(q, np.float64)
@@ -49,24 +85,11 @@ def blockwise_attention(q, k, v, Br: int, Bc: int, scale: float | None = None,
     out = np.zeros((Nq, v.shape[1]))
     lse = np.full(Nq, -np.inf)
     for i0 in range(0, Nq, Br):
-        qi = q[i0:i0 + Br]
-        m = np.full(qi.shape[0], -np.inf)
-        l = np.zeros(qi.shape[0])
-        O = np.zeros((qi.shape[0], v.shape[1]))
-        for j0 in range(0, Nk, Bc):
-            S = (qi @ k[j0:j0 + Bc].T) * scale
-            if causal:
-                hidden = kp[None, j0:j0 + Bc] > qp[i0:i0 + Br, None]
-                S = np.where(hidden, -np.inf, S)
-            m_new = np.maximum(m, S.max(axis=1))
-            alpha = _exp_shift(m, m_new)
-            P = _exp_shift(S, m_new[:, None])
-            l = alpha * l + P.sum(axis=1)
-            O = alpha[:, None] * O + P @ v[j0:j0 + Bc]
-            m = m_new
-        seen = l > 0
-        out[i0:i0 + Br][seen] = O[seen] / l[seen, None]
-        lse[i0:i0 + Br][seen] = m[seen] + np.log(l[seen])
+        rows = slice(i0, min(Nq, i0 + Br))
+        tiles = [(k[j0:j0 + Bc], v[j0:j0 + Bc],
+                  (kp[None, j0:j0 + Bc] > qp[rows, None]) if causal else None)
+                 for j0 in range(0, Nk, Bc)]
+        out[rows], lse[rows] = _stream_tiles(q[rows], tiles, scale)
     return out, lse
 
 
@@ -99,15 +122,14 @@ def ring_simulation(q, k, v, n_devices: int, direction: int = -1):
 
 
 def sigmoid_merge(out, lse, block_out, block_lse):
-    """The Twinkle page's ``update_out_and_lse`` in its sigmoid form:
-
-        out <- out - sigmoid(block_lse - lse) * (out - block_out)
-        lse <- lse - logsigmoid(lse - block_lse)
-
-    Taken literally the second line gives NaN when lse = -inf; the reading used
-    here: an empty side (lse = -inf) contributes nothing, so the other side is
-    returned unchanged, and two empty sides stay empty (out 0, lse -inf).
-    out: [n, d], lse: [n].
+    """The log-sum-exp merge in the logistic form of the Twinkle page's
+    ``update_out_and_lse``: with a = lse and b = block_lse, the merged output
+    is the convex combination sigma(a - b) out + sigma(b - a) block_out
+    (sigma the logistic function) and the merged lse is a + softplus(b - a).
+    Read literally the page's form is NaN when a side is -inf; the reading
+    used here: an empty side (lse = -inf) contributes nothing, so the other
+    side is returned unchanged, and two empty sides stay empty (out 0,
+    lse -inf).  out: [n, d], lse: [n].
     """
     out = np.array(out, np.float64)
     lse = np.array(lse, np.float64)
@@ -116,12 +138,12 @@ def sigmoid_merge(out, lse, block_out, block_lse):
     a_empty = np.isneginf(lse)
     b_empty = np.isneginf(block_lse)
     both = ~a_empty & ~b_empty
-    diff = block_lse[both] - lse[both]
-    sig = 1.0 / (1.0 + np.exp(-diff))
-    out[both] = out[both] - sig[:, None] * (out[both] - block_out[both])
-    # -logsigmoid(x) = log(1 + exp(-x)) with x = lse - block_lse, written stably
-    x = lse[both] - block_lse[both]
-    lse[both] = lse[both] + np.where(x > 0, np.log1p(np.exp(-x)), -x + np.log1p(np.exp(x)))
+    t = block_lse[both] - lse[both]
+    w_b = 1.0 / (1.0 + np.exp(-t))          # sigma(b - a)
+    w_a = 1.0 / (1.0 + np.exp(t))           # sigma(a - b)
+    out[both] = w_a[:, None] * out[both] + w_b[:, None] * block_out[both]
+    softplus = np.maximum(t, 0.0) + np.log1p(np.exp(-np.abs(t)))
+    lse[both] = lse[both] + softplus
     take_b = a_empty & ~b_empty
     out[take_b] = block_out[take_b]
     lse[take_b] = block_lse[take_b]
@@ -180,40 +202,32 @@ def zigzag_ring_forward(q_shards, k_shards, v_shards, W: int, rank: int,
 
 
 def online_softmax_over_blocks(q, k_blocks, v_blocks, scale: float | None = None):
-    """The guijiagi.com page's online softmax (one pass over key/value blocks,
-    running m, l and o rescaled by exp(m - m_new), division at the end),
-    for a matrix of query rows and key/value blocks in the order given.
+    """One pass of the online softmax over key/value blocks in the order
+    given (the guijiagi.com page's online-softmax section: a running max and
+    sum, a rescaling factor exp(m - m_new), the division at the end), for a
+    matrix of query rows; the recurrence is ``_stream_tiles``.
     Returns (O [Nq, d], lse [Nq])."""
     q = np.asarray(q, np.float64)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[1])
-    m = np.full(q.shape[0], -np.inf)
-    l = np.zeros(q.shape[0])
-    o = np.zeros((q.shape[0], np.asarray(v_blocks[0]).shape[1]))
-    for kb, vb in zip(k_blocks, v_blocks):
-        s = (q @ np.asarray(kb, np.float64).T) * scale
-        m_new = np.maximum(m, s.max(axis=1))
-        alpha = _exp_shift(m, m_new)
-        o = o * alpha[:, None]
-        l = l * alpha
-        p = _exp_shift(s, m_new[:, None])
-        o = o + p @ np.asarray(vb, np.float64)
-        l = l + p.sum(axis=1)
-        m = m_new
-    return o / l[:, None], m + np.log(l)
+    tiles = [(np.asarray(kb, np.float64), np.asarray(vb, np.float64), None)
+             for kb, vb in zip(k_blocks, v_blocks)]
+    return _stream_tiles(q, tiles, scale)
 
 
 def ring_backward(q, k, v, o, lse, do, W: int, rank: int, scale: float | None = None):
     """The ring backward of one device, simulated: gradients of the device's
     query block and of every key/value block, non-causal.
 
-    Follows the youngju.dev ``ring_attention_backward`` description: the
-    device first forms D = rowsum(dO * O) from its saved output; then at each
-    of the W steps it holds the key/value block of device (rank - step) mod W,
-    recomputes S = scale Q K^T and P = exp(S - lse) from the saved log-sum-exp,
-    and forms dV_blk = P^T dO, dP = dO V^T, dS = P (dP - D) scale,
-    dQ += dS K, dK_blk = dS^T Q.  The block gradients go back to the block's
-    owner, which sums what every device sends it.
+    What the youngju.dev ring backward relies on, written as whole matrices:
+    the probabilities are recomputed from the saved log-sum-exp,
+    P = exp(scale Q K^T - lse), and the gradient of sum(dO * O) with respect
+    to the scaled scores is G = P * (dO V^T - D) with D = rowsum(dO * O)
+    taken from the saved output.  Then dQ = scale G K, dK = scale G^T Q and
+    dV = P^T dO.  The ring splits the keys into W blocks: at step s the
+    device holds block (rank - s) mod W and adds that block's columns of G
+    and P to dQ, and forms that block's dK and dV, which go back to the
+    block's owner (here: written into the rows of the block).
 
     q, o, do: [Nq, d] (this device's query block), lse [Nq]; k, v: [Nk, d]
     (the whole sequence, W equal blocks).  Returns (dQ [Nq, d], dK, dV [Nk, d])
@@ -226,21 +240,17 @@ def ring_backward(q, k, v, o, lse, do, W: int, rank: int, scale: float | None = 
         scale = 1.0 / math.sqrt(d)
     if Nk % W:
         raise ValueError("Nk must be a multiple of W")
-    S_blk = Nk // W
-    D = (do * o).sum(axis=1, keepdims=True)
+    blk = Nk // W
+    P = _exp_shift(scale * (q @ k.T), lse[:, None])
+    G = P * (do @ v.T - (do * o).sum(axis=1, keepdims=True))
     dQ = np.zeros_like(q)
     dK = np.zeros_like(k)
     dV = np.zeros_like(v)
     for step in range(W):
-        src = (rank - step) % W
-        rows = slice(src * S_blk, (src + 1) * S_blk)
-        Kb, Vb = k[rows], v[rows]
-        P = _exp_shift((q @ Kb.T) * scale, lse[:, None])
-        dV[rows] += P.T @ do
-        dP = do @ Vb.T
-        dS = P * (dP - D) * scale
-        dQ += dS @ Kb
-        dK[rows] += dS.T @ q
+        cols = slice(((rank - step) % W) * blk, ((rank - step) % W + 1) * blk)
+        dQ += scale * (G[:, cols] @ k[cols])
+        dK[cols] = scale * (G[:, cols].T @ q)
+        dV[cols] = P[:, cols].T @ do
     return dQ, dK, dV
 
 

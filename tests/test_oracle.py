@@ -291,7 +291,7 @@ def test_block_size_invariance(causal):
     out, lse = oracle.attention(q[None, :, None], k[None, :, None], v[None, :, None],
                                 causal=causal)
     for Br, Bc in itertools.product([1, 3, 5, 8, 16, 32], repeat=2):
-        bo, bl = recurrences.blockwise_attention(q, k, v, Br, Bc, causal=causal)
+        bo, bl = recurrences.tiled_online_softmax(q, k, v, Br, Bc, causal=causal)
         assert np.allclose(bo, out[0, :, 0], rtol=0, atol=1e-12), (Br, Bc)
         assert np.allclose(bl, lse[0, :, 0], rtol=0, atol=1e-12), (Br, Bc)
 
