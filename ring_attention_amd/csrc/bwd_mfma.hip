@@ -52,15 +52,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 // Buffer form of dma16: 16 bytes per lane from a raw buffer resource plus a
@@ -78,10 +78,10 @@ __device__ __forceinline__ v4i tensor_rsrc(const void* base) {
 }
 // soff: the wave-uniform part of the offset (scalar), voff: the lane part
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t soff, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

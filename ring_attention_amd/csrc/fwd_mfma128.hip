@@ -10,8 +10,8 @@
 // Schedule.  A workgroup of 8 wavefronts owns 256 query rows, 32 per wave;
 // waves w and w+4 share a SIMD.  Waves 0-3 form group A, waves 4-7 group B.
 // Per key tile k each group runs an MFMA phase M_k = {PV of tile k-1, QK of
-// tile k} (32 MFMAs) and a VALU phase V_k = {mask, max, exp, sum, P} of tile
-// k.  Group B runs one phase behind group A, so one group's softmax runs
+// tile k} (32 MFMAs) and a VALU phase V_k = {mask, exp, sum, P; the row max
+// only when the sum shows it can move} of tile k.  Group B runs one phase behind group A, so one group's softmax runs
 // next to the other group's matrix work on every SIMD:
 //      window   0  |  1  |   2    |   3    |  ...
 //      A        M0 | V0  | M1  V1 | M2  V2 |
@@ -32,12 +32,14 @@
 // c ^ (r%16), V at c ^ 4(r%4)) so the fragment reads below are conflict-free.
 // S^T = K Q^T with v_mfma_f32_32x32x16 (A = K fragment, B = Q held in
 // registers); O^T = V^T P^T with the V^T fragment from two ds_read_b64_tr_b16
-// transposing reads and P taken straight from the score registers (register
-// r of lane l holds key 8(r/4) + 4(l/32) + r%4 of a 32-key block).
+// transposing reads and P packed from the score registers in place (register
+// r of lane l holds key 8(r/4) + 4(l/32) + r%4 of a 32-key block), so it is
+// the B operand as it stands.
 // The DMA is issued from inline assembly and waited for explicitly
 // (s_waitcnt vmcnt) before the barrier that precedes its first reader, so
 // the compiler adds no conservative waits between a DMA and unrelated LDS
-// reads.  Nothing else in this kernel uses M0.
+// reads.  The LDS address is an M0 operand of the asm, so the compiler
+// writes M0 itself and knows the asm reads it.
 #include <type_traits>
 
 #include "kcommon.h"
@@ -73,9 +75,9 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 // buffer form, with one resource per key/value head, measured 2.5% faster on
 // the ring share; it is used when a head's rows span less than 4 GB.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -90,9 +92,9 @@ __device__ __forceinline__ v4i head_rsrc(const char* base) {
   return r;
 }
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -277,10 +279,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
 
   // per-group state carried between phases
   // sacc holds this wave's scores of the last scored tile; the V phase
-  // replaces them with P in the input type, packed into sacc[0] (key pair
-  // (r, r+1) of 32-key block kb -> dword 8 kb + r/2), which the next PV
-  // reads.  P = 0 when the wave did not score the tile.
+  // writes their P in the input type, packed into pk (key pair (r, r+1) of
+  // 32-key block kb -> dword 8 kb + r/2), which the next PV reads as its
+  // B operand.  P = 0 when the wave did not score the tile.
   f32x16 sacc[NKB];
+  f32x16 pk = f32x16{};
   static_assert(NKB == 2, "P of a 64-key tile fills exactly one accumulator");
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
@@ -318,8 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
       if (i + kAhead < N) fb[i % kAhead] = load(i + kAhead);
       if (PV && i < NPV) {
         const int u = i / DB;
-        const f32x4 pw = {sacc[0][4 * u], sacc[0][4 * u + 1], sacc[0][4 * u + 2],
-                          sacc[0][4 * u + 3]};
+        const f32x4 pw = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
         oacc[i % DB] = TT::mfma32x32x16(a, __builtin_bit_cast(v8, pw), oacc[i % DB]);
       } else {
         const int j = i - NPV;
@@ -356,14 +358,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
     const bool s_live = wave_active && (!s.causal || s_kpos0 <= wave_qhi);
     cursor_next<BC>(cqk, s, qt.rank, qhi);
     if (!s_live) {
-      sacc[0] = f32x16{};  // P = 0
+      pk = f32x16{};  // P = 0
       return;
     }
     const bool need_mask = s_krows < BC || (s.causal && s_kpos0 + s_krows - 1 > wave_qlo);
+    bool sees_key = true;  // this lane's query has a visible key in the tile
     if (need_mask) {
       // key index of register r of block kb is kb*32 + 8(r/4) + 4hl + r%4;
       // compare its lane-independent part against the limit shifted by 4hl
-      const int lim = visible_limit(s_krows, s.causal, q_pos - s_kpos0) - 4 * hl;
+      const int vis = visible_limit(s_krows, s.causal, q_pos - s_kpos0);
+      sees_key = vis > 0;
+      const int lim = vis - 4 * hl;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -372,36 +377,54 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
           sacc[kb][r] = kk2 < lim ? sacc[kb][r] : kNegInf;
         }
     }
-    float mt = kNegInf;
+    // P = exp2(c s - m) into pk (input type, packed), its fp32 row sum into
+    // four partial sums; the scores stay in sacc for the slow path below.
+    float tsum;
+    auto exps = [&](float m_use) {
+      float rs[4];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-    mt = pair_max(mt);
-    const float m_cand = mt * p.c;
-    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, m_cand);
-      const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
-      m_run = m_new;
-      l_run *= alpha;
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = exp2_fast(fmaf(sacc[kb][r], p.c, -m_use));
+          const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], p.c, -m_use));
+          const int i = (r >> 1) & 3;
+          rs[i] = (kb == 0 && r < 8) ? p0 : rs[i] + p0;
+          rs[i] += p1;
+          const E2 pair = {to_elem<TT>(p0), to_elem<TT>(p1)};
+          pk[8 * kb + r / 2] = __builtin_bit_cast(float, pair);
+        }
+      tsum = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    };
+    // Lazy rescaling: the running max m moves only when a score exceeds it
+    // by more than kRescaleSlack (base-2 units), i.e. when some p would
+    // exceed 2^kRescaleSlack.  Every p is >= 0, so a lane whose sum stays
+    // within half that bound holds no such p, and the exact row max is
+    // needed only when some lane's sum does not (or a row sees its first
+    // key); the decisions, and so the results, are those of computing the
+    // max for every tile.
+    const bool no_max = m_run == kNegInf;
+    exps(no_max ? 0.f : m_run);
+    const bool slow = (tsum > 0.5f * kRescaleBound) | (no_max & sees_key);
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+      float mt = kNegInf;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    // l sums P in fp32 (before rounding), four partial sums
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+      mt = pair_max(mt);
+      const float m_cand = mt * p.c;
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, m_cand);
+        const float alpha = exp2_fast(m_run - (m_new == kNegInf ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_fast(fmaf(sacc[kb][r], p.c, -m_use));
-        const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], p.c, -m_use));
-        rs[(r >> 1) & 3] += p0;
-        rs[(r >> 1) & 3] += p1;
-        const E2 pair = {to_elem<TT>(p0), to_elem<TT>(p1)};
-        sacc[0][8 * kb + r / 2] = __builtin_bit_cast(float, pair);
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        exps(m_run == kNegInf ? 0.f : m_run);
       }
-    l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
+    l_run += tsum;
   };
 
   // Before the window in which the groups score tile j, tile j must have

@@ -100,6 +100,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // Lazy rescaling threshold, in base-2 units of the scaled score.
 constexpr float kRescaleSlack = 8.f;
+constexpr float kRescaleBound = 256.f;  // 2^kRescaleSlack
 
 // Number of leading keys of a key tile visible to one query: keys kk < limit
 // are visible.  `rows` keys are present in the tile; under the causal rule
