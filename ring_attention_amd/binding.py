@@ -8,7 +8,6 @@ fallback: if the library is missing or a call fails, an exception is raised.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -55,11 +54,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
                               i32, i32, i32, i32, vp]
     lib.rattn_fwd_step.restype = i32
-    lib.rattn_fwd_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
-                                   i32, i64p, i64p, i64p, i64p, vp]
+    lib.rattn_fwd_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i64, i64, i64,
+                                   i64, i32, i32, f32, i32, i64p, i64p, i64p, i64p, vp]
     lib.rattn_fwd_step_merge.restype = i32
-    lib.rattn_fwd_step_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32,
-                                         f32, i32, i64p, i64p, i64p, i64p, i64, i64, vp]
+    lib.rattn_fwd_step_merge.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i64, i64,
+                                         i64, i64, i32, i32, f32, i32, i64p, i64p, i64p, i64p,
+                                         i64, i64, vp]
     lib.rattn_merge.restype = i32
     lib.rattn_merge.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, vp]
     lib.rattn_fwd_varlen.restype = i32
@@ -196,14 +196,28 @@ def _segs(pairs):
     return starts, lens
 
 
+def _rows(segs, off, total, what):
+    """Rows a step reads: the segment lengths, from row `off` of `total`."""
+    n = sum(int(p[1]) for p in segs)
+    if off < 0 or off + n > total:
+        raise ValueError(f"{what} rows [{off}, {off + n}) exceed the tensor's {total} rows")
+    return n
+
+
 def fwd_step_merge(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, causal: bool,
                    q_segs, k_segs, out: torch.Tensor, lse: torch.Tensor, row_off: int = 0,
-                   scale: float | None = None):
+                   scale: float | None = None, q_off: int = 0, k_off: int = 0):
     """One ring step merged into the running float32 (out, lse) at rows
-    [row_off, row_off + Nq) (rattn_fwd_step_merge); returns (out, lse)."""
+    [row_off, row_off + Nq) (rattn_fwd_step_merge); returns (out, lse).
+
+    The step reads query rows [q_off, q_off + Nq) of q and key/value rows
+    [k_off, k_off + Nk) of k_blk, v_blk, Nq and Nk being the segment lengths'
+    sums (no copy of a part of a shard)."""
     _qkv(q, k_blk, v_blk)
-    B, Nq, Hq, d = q.shape
-    Nk, Hkv = k_blk.shape[1], k_blk.shape[2]
+    B, q_rows, Hq, d = q.shape
+    k_rows, Hkv = k_blk.shape[1], k_blk.shape[2]
+    Nq = _rows(q_segs, q_off, q_rows, "query")
+    Nk = _rows(k_segs, k_off, k_rows, "key")
     for name, t in (("out", out), ("lse", lse)):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous float32 tensor on q's device")
@@ -214,23 +228,28 @@ def fwd_step_merge(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, ca
     kst, kl = _segs(k_segs)
     rc = load_library().rattn_fwd_step_merge(
         q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
-        Hkv, Nq, Nk, d, DTYPE_CODES[q.dtype], _scale(scale), int(bool(causal)), qs, ql, kst, kl,
-        out.shape[1], int(row_off), _stream(q))
+        Hkv, q_rows, int(q_off), Nq, k_rows, int(k_off), Nk, d, DTYPE_CODES[q.dtype],
+        _scale(scale), int(bool(causal)), qs, ql, kst, kl, out.shape[1], int(row_off),
+        _stream(q))
     _check("rattn_fwd_step_merge", rc)
     return out, lse
 
 
 def fwd_step(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, causal: bool,
              q_segs, k_segs, scale: float | None = None,
-             out_part: torch.Tensor | None = None, lse_part: torch.Tensor | None = None):
+             out_part: torch.Tensor | None = None, lse_part: torch.Tensor | None = None,
+             q_off: int = 0, k_off: int = 0):
     """One ring step (rattn_fwd_step): normalised float32 partial and its lse.
 
-    q_segs / k_segs: up to two (start_position, length) pairs covering the rows
-    of q / k_blk in order.
+    q_segs / k_segs: up to two (start_position, length) pairs covering, in
+    order, the query rows [q_off, q_off + Nq) of q and the key/value rows
+    [k_off, k_off + Nk) of k_blk, v_blk (Nq, Nk: the lengths' sums).
     """
     _qkv(q, k_blk, v_blk)
-    B, Nq, Hq, d = q.shape
-    Nk, Hkv = k_blk.shape[1], k_blk.shape[2]
+    B, q_rows, Hq, d = q.shape
+    k_rows, Hkv = k_blk.shape[1], k_blk.shape[2]
+    Nq = _rows(q_segs, q_off, q_rows, "query")
+    Nk = _rows(k_segs, k_off, k_rows, "key")
     qs, ql = _segs(q_segs)
     kst, kl = _segs(k_segs)
     if out_part is None:
@@ -239,7 +258,8 @@ def fwd_step(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor, causal: 
         lse_part = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
     lib = load_library()
     rc = lib.rattn_fwd_step(q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
-                            out_part.data_ptr(), lse_part.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+                            out_part.data_ptr(), lse_part.data_ptr(), B, Hq, Hkv, q_rows,
+                            int(q_off), Nq, k_rows, int(k_off), Nk, d,
                             DTYPE_CODES[q.dtype], _scale(scale), int(bool(causal)),
                             qs, ql, kst, kl, _stream(q))
     _check("rattn_fwd_step", rc)
@@ -263,10 +283,6 @@ def merge(out: torch.Tensor, lse: torch.Tensor, blk_out: torch.Tensor, blk_lse: 
                          B, H, Nq, Nb, int(row_off), d, _stream(out))
     _check("rattn_merge", rc)
     return out, lse
-
-
-def default_scale(d: int) -> float:
-    return 1.0 / math.sqrt(d)
 
 
 def _like(name, t, ref, dtype=None):
