@@ -3,23 +3,25 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-one simulated device's share of an 8-way ZigZag causal ring at its real shape
-(total sequence 131072 in 16 chunks of 8192, the device's query shard =
-chunks {2, 13}, 8 heads, d = 128, bf16, N(0,1)), run as the ring runs it:
-8 step-kernel launches over the 8 key/value shards in ring order; after the
-first, each merges its result into the running output with the log-sum-exp
-correction in its epilogue (steps_separate_merge times the same ring with the
-merges as launches of their own).
+the long-context GQA causal workload (batch 1, 524288 tokens, 32 query heads
+over 8 key/value heads, d = 128, bf16, N(0,1)) processed as the 8-device
+ZigZag ring schedule (16 chunks of 32768) of every device in one launch of
+rattn_fwd: every query tile walks its device's key/value chunks in ring order,
+skips fully masked tiles, masks the diagonal ones, keeps the online softmax
+in registers and merges the ring steps in place (one running max, sum and
+accumulator per row), dividing by the sum once at the end.
 
 `value` is causal-adjusted TFLOP/s: 4*d FLOP per visible (query, key) pair
 per query head (2d for QK^T, 2d for PV; exponentials and masked work are not
 counted), pairs counted from the positions alone.  Timing uses HIP events on
 the stream the kernels run on; inputs are resident in HBM before timing.
 
-Also reported: the roofline entry of the dominant kernel (the step kernel,
-MFMA bound, against the 2.5 PFLOP/s dense bf16 peak), the fp64 CPU oracle
-timed on a bounded sample of the same workload, and other workloads timed
-the same way (extras).
+Also reported: the roofline entry of the dominant kernel (MFMA bound, against
+the 2.5 PFLOP/s dense bf16 peak, and that peak restated from the device's CU
+count and clock), the fp64 CPU oracle timed on a bounded sample of the same
+workload, and other workloads timed the same way (extras), among them one
+device's share of the 131072-token ZigZag ring run as 8 ring-step launches
+with the log-sum-exp merge in their epilogues (with its own roofline entry).
 """
 from __future__ import annotations
 
@@ -38,24 +40,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
-STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, true, true>"  # d=128 16-bit path, fp32 partials
-# sources the step kernel is built from; the stored counter summary is valid
+MFMA_BF16_FLOP_PER_CLK_CU = 4096  # 4 SIMDs x one 32x32x16 bf16 MFMA (32768 FLOP) per 32 clocks
+# the dominant kernel of the headline workload (d = 128, 16-bit, output in the input type)
+HEADLINE_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, false, true>"
+# the ring-step kernel (d = 128, 16-bit, float32 partials merged in the epilogue)
+STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, true, true>"
+# sources the d = 128 kernel is built from; a stored counter summary is valid
 # only for the kernel it was measured on
 KERNEL_SOURCES = ("fwd_mfma128.hip", "kcommon.h", "ring_sched.h", "launch.h")
+HEADLINE_COUNTERS = os.path.join(ROOT, "profiles",
+                                 "fwd_mfma128_gqa_causal_512k_bf16_hbm_counters.txt")
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles",
                                "fwd_mfma128_zigzag_rank2_131k_bf16_hbm_counters.txt")
+HEADLINE_WORKLOAD = 5
 METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 MI355X"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=8192,
+    ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="query rows of the workload the CPU oracle times")
+    ap.add_argument("--kernel", default=None,
+                    help="kernel the --summarize-counters / --summarize-mfma summaries are "
+                         "about (default: the headline workload's kernel)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose byte "
                          "counters calibrate the kernels' FETCH_SIZE/WRITE_SIZE readings")
@@ -66,6 +78,9 @@ def parse():
                     help="run only the causal layout comparison and print its JSON")
     ap.add_argument("--bwd-only", action="store_true",
                     help="run only the backward measurements and print their JSON")
+    ap.add_argument("--ring-share-only", action="store_true",
+                    help="run only the 131072-token ZigZag ring share (ring steps, fused) "
+                         "and print its JSON")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
     ap.add_argument("--summarize-step-dispatches", metavar="KERNEL_TRACE_CSV",
@@ -135,7 +150,7 @@ def _counter_means(path: str, counter: str):
     return per
 
 
-def summarize_counters(fetch_csv: str, write_csv: str) -> None:
+def summarize_counters(fetch_csv: str, write_csv: str, kernel: str) -> None:
     """HBM bytes per launch of the step kernel from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the 1 GiB copy of
     --copy-probe (the largest copy dispatch in the run)."""
@@ -145,28 +160,28 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     copy_f = max(v for n, vs in fetch.items() if "copy" in n for v in vs)
     copy_w = max(v for n, vs in write.items() if "copy" in n for v in vs)
     f_scale, w_scale = gib_kib / copy_f, gib_kib / copy_w
-    kf, kw = fetch[STEP_KERNEL], write[STEP_KERNEL]
+    kf, kw = fetch[kernel], write[kernel]
     fetch_b = sum(kf) / len(kf) * 1024 * f_scale
     write_b = sum(kw) / len(kw) * 1024 * w_scale
-    print(f"kernel: {STEP_KERNEL}")
+    print(f"kernel: {kernel}")
     print(f"kernel_source_sha256_16: {kernel_source_hash()}")
     print(f"copy_probe_fetch_kib: {copy_f:.0f}  (1 GiB copy; scale {f_scale:.4f})")
     print(f"copy_probe_write_kib: {copy_w:.0f}  (1 GiB copy; scale {w_scale:.4f})")
-    print(f"step_kernel_dispatches: {len(kf)} {len(kw)}")
-    print(f"step_kernel_fetch_kib_avg: {sum(kf) / len(kf):.1f}")
-    print(f"step_kernel_write_kib_avg: {sum(kw) / len(kw):.1f}")
-    print(f"step_kernel_hbm_read_bytes_per_launch: {fetch_b:.0f}")
-    print(f"step_kernel_hbm_write_bytes_per_launch: {write_b:.0f}")
-    print(f"step_kernel_hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
+    print(f"kernel_dispatches: {len(kf)} {len(kw)}")
+    print(f"kernel_fetch_kib_avg: {sum(kf) / len(kf):.1f}")
+    print(f"kernel_write_kib_avg: {sum(kw) / len(kw):.1f}")
+    print(f"kernel_hbm_read_bytes_per_launch: {fetch_b:.0f}")
+    print(f"kernel_hbm_write_bytes_per_launch: {write_b:.0f}")
+    print(f"kernel_hbm_bytes_per_launch: {fetch_b + write_b:.0f}")
 
 
-def summarize_mfma(path: str) -> None:
+def summarize_mfma(path: str, kernel: str) -> None:
     """Matrix-core utilisation of the step kernel: SQ_VALU_MFMA_BUSY_CYCLES over
     the SIMD-cycles of the dispatch (GRBM_GUI_ACTIVE is summed over the 8 XCDs,
     each with 32 CUs x 4 SIMDs), plus instruction counts per dispatch."""
     per, dur = {}, {}
     for r in csv.DictReader(open(path)):
-        if _short_name(r["Kernel_Name"]) != STEP_KERNEL:
+        if _short_name(r["Kernel_Name"]) != kernel:
             continue
         key = r["Dispatch_Id"]
         per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
@@ -176,7 +191,7 @@ def summarize_mfma(path: str) -> None:
     t = sum(dur.values()) / n
     xcd_cycles = avg["GRBM_GUI_ACTIVE"] / 8
     simd_cycles = xcd_cycles * 8 * 32 * 4
-    print(f"kernel: {STEP_KERNEL}")
+    print(f"kernel: {kernel}")
     print(f"kernel_source_sha256_16: {kernel_source_hash()}")
     print(f"dispatches: {n}")
     print(f"avg_duration_us: {t * 1e6:.1f}")
@@ -225,18 +240,18 @@ def summarize_kernels(fetch_csv: str, write_csv: str, sq_csv: str) -> None:
               f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:9.4f} {avg['SQ_INSTS_VALU']:15.4g}")
 
 
-def stored_traffic():
-    """HBM bytes per step-kernel launch from the committed counter summary, or None
-    when it is missing or was measured on other kernel sources."""
+def stored_traffic(path: str):
+    """HBM bytes per launch of a kernel from a committed counter summary, or
+    None when it is missing or was measured on other kernel sources."""
     try:
         kv = {}
-        for line in open(COUNTER_SUMMARY):
+        for line in open(path):
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 kv[key.strip()] = val.split()[0] if val.split() else ""
         if kv.get("kernel_source_sha256_16") != kernel_source_hash():
             return None
-        return int(kv["step_kernel_hbm_bytes_per_launch"])
+        return int(kv["kernel_hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -322,6 +337,157 @@ def step_plan(N, W, rank, c):
     return plan
 
 
+def device_peak(torch):
+    """The dense bf16 MFMA peak restated from the device: CU count x peak
+    engine clock x 4096 FLOP per clock per CU (four SIMDs, each finishing one
+    32x32x16 bf16 MFMA of 32768 FLOP every 32 clocks).  The clock comes from
+    hipDeviceGetAttribute of the HIP runtime this process already uses."""
+    import ctypes
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clk_khz = None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate = 5, hipDeviceAttributeMultiprocessorCount = 63
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0 and 5e5 < val.value < 5e6:
+            clk_khz = val.value
+        cu = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(cu), 63, 0) != 0 or cu.value != cus:
+            clk_khz = None
+    except OSError:
+        pass
+    out = {"published_tflops": PEAK_BF16_TFLOPS, "compute_units": cus,
+           "peak_clock_mhz": None if clk_khz is None else clk_khz / 1000,
+           "flop_per_clock_per_cu": MFMA_BF16_FLOP_PER_CLK_CU, "from_cus_x_clock_tflops": None}
+    if clk_khz is not None:
+        out["from_cus_x_clock_tflops"] = round(
+            cus * clk_khz * 1e3 * MFMA_BF16_FLOP_PER_CLK_CU / 1e12, 1)
+    return out
+
+
+def headline(torch, binding, workloads, dev, args):
+    """The long-context GQA causal workload: one rattn_fwd launch per step
+    (every device's ZigZag ring schedule), W warm-up steps, K timed steps."""
+    w = workloads.workload(HEADLINE_WORKLOAD)
+    need = 2 * (w.B * w.Nq * w.Hq * w.d) * 2 + 2 * (w.B * w.N * w.Hkv * w.d) * 2 \
+        + w.B * w.Nq * w.Hq * 4
+    free, _total = torch.cuda.mem_get_info(dev)
+    if free < need * 1.05:
+        print(f"bench.py: the {w.name} workload needs {need / 1e9:.1f} GB of device memory, "
+              f"{free / 1e9:.1f} GB are free", file=sys.stderr)
+        sys.exit(1)
+    q, k, v = workloads.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    pairs = w.N * (w.N + 1) // 2  # per head: keys 0..i for query i
+    flop = 4 * w.d * w.Hq * w.B * pairs
+
+    def step():
+        return binding.fwd(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=-1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    # per-launch HIP events around each call on the stream it runs on (torch's
+    # current stream, which the binding passes): one launch of the dominant
+    # kernel per step
+    kern = Timer(torch)
+    for _ in range(args.steps):
+        kern(step)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in kern.pairs) if kern.total_ms() else []
+    avg_launch = sum(launch_ms) / len(launch_ms)
+    return w, (q, k, v), flop, pairs, ms_per_step, launch_ms, avg_launch
+
+
+def ring_share_extra(torch, binding, ring, workloads, dev, args, peak):
+    """One simulated device's share of the 8-way ZigZag causal ring over
+    131072 tokens (chunks {2, 13}, 8 heads): the device's 8 ring-step launches
+    in ring order, steps 2-8 merging into the running (out, lse) in their
+    epilogue; the same ring with separate merge launches; the same share in
+    one fused rattn_fwd launch.  Carries the step kernel's roofline entry."""
+    w = workloads.workload(4)
+    W, rank, N, d, Hq = w.W, w.rank, w.N, w.d, w.Hq
+    c = N // (2 * W)
+    q, k, v = workloads.make_inputs(w, device=dev)
+    ks = [ring.shard(k, W, True, r) for r in range(W)]
+    vs = [ring.shard(v, W, True, r) for r in range(W)]
+    torch.cuda.synchronize()
+    plan = step_plan(N, W, rank, c)
+    pairs = sum(causal_pairs(runs_positions(qr), runs_positions(kr)) for qr, kr in plan)
+    flop = 4 * d * Hq * w.B * pairs
+    reps = max(10, 2 * args.steps)
+
+    def one(hook=None, fused_merge=True):
+        kw = {} if hook is None else {"hook": hook}
+        return ring.ring_forward_steps(q, ks, vs, W, True, rank, causal=True,
+                                       fused_merge=fused_merge, **kw)
+    warm_up(torch, one, 3)
+    ms = loop_ms(torch, one, reps)
+    kern, merge_t = Timer(torch), Timer(torch)
+
+    def hook(kind, fn):
+        return (kern if kind == "step" else merge_t)(fn)
+    for _ in range(reps):
+        one(hook)
+    kern_ms = kern.total_ms() / len(kern.pairs)
+    flop_launch = flop / len(plan)
+    achieved = flop_launch / (kern_ms * 1e-3) / 1e12
+    warm_up(torch, lambda: one(fused_merge=False), 3)
+    sep_ms = loop_ms(torch, lambda: one(fused_merge=False), reps)
+    merge_t.pairs.clear()
+    for _ in range(reps):
+        one(hook, fused_merge=False)
+    merge_ms = merge_t.total_ms() / max(1, len(merge_t.pairs))
+
+    def fused():
+        return binding.fwd(q, k, v, causal=True, n_ring_steps=W, zigzag=True, rank=rank)
+    warm_up(torch, fused, 3)
+    fused_ms = loop_ms(torch, fused, reps)
+    res = {
+        "ring_steps": {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                       "pct_of_peak": round(100 * flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                       "mode": "8 ring-step launches; steps 2-8 merge into the running "
+                               "(out, lse) in the kernel epilogue"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic(COUNTER_SUMMARY), "kernel": STEP_KERNEL,
+                     "avg_launch_ms": round(kern_ms, 4), "launches": len(kern.pairs),
+                     "flop_per_launch": flop_launch},
+        "steps_separate_merge": {"ms": round(sep_ms, 4),
+                                 "tflops": round(flop / (sep_ms * 1e-3) / 1e12, 2),
+                                 "merge_avg_ms": round(merge_ms, 4)},
+        "fused": {"ms": round(fused_ms, 4), "tflops": round(flop / (fused_ms * 1e-3) / 1e12, 2),
+                  "pct_of_peak": round(100 * flop / (fused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                       2)},
+        "visible_pairs_per_head": pairs, "flop": flop,
+        "conventional_flop": 4 * d * Hq * w.B * w.Nq * N // 2,
+    }
+    del q, k, v, ks, vs
+    torch.cuda.empty_cache()
+    return {w.name: res}
+
+
+def tiny_latency_extra(torch, binding, workloads, dev, args):
+    """The 4-device x 8-token ring simulation (fp32, d = 16): latency of one
+    rattn_fwd call in microseconds (back-to-back calls under one event pair)."""
+    w = workloads.workload(1)
+    q, k, v = workloads.make_inputs(w, device=dev)
+
+    def run():
+        return binding.fwd(q, k, v, causal=False, n_ring_steps=w.W, zigzag=False, rank=-1)
+    warm_up(torch, run, 10)
+    ms = loop_ms(torch, run, 200)
+    return {w.name: {"us_per_call": round(ms * 1e3, 2),
+                     "note": "latency bound: 32 query rows, one workgroup"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -332,13 +498,13 @@ def main():
         summarize_stats(args.summarize_stats)
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, args.kernel or HEADLINE_KERNEL)
         return
     if args.summarize_step_dispatches:
         summarize_step_dispatches(args.summarize_step_dispatches, args)
         return
     if args.summarize_mfma:
-        summarize_mfma(args.summarize_mfma)
+        summarize_mfma(args.summarize_mfma, args.kernel or HEADLINE_KERNEL)
         return
     if args.summarize_kernels:
         summarize_kernels(*args.summarize_kernels)
@@ -372,78 +538,15 @@ def main():
         print(json.dumps({"extras": backward_extras(torch, binding, ring, workloads, dev, args)}),
               flush=True)
         return
-    w = workloads.workload(4)
-    W, rank, N, d, Hq = w.W, w.rank, w.N, w.d, w.Hq
-    c = N // (2 * W)
-    q, k, v = workloads.make_inputs(w, device=dev)
-    ks = [ring.shard(k, W, True, r) for r in range(W)]
-    vs = [ring.shard(v, W, True, r) for r in range(W)]
-    torch.cuda.synchronize()
-
-    plan = step_plan(N, W, rank, c)
-    step_pairs = [causal_pairs(runs_positions(qr), runs_positions(kr)) for qr, kr in plan]
-    pairs = sum(step_pairs)
-    flop_per_step = 4 * d * Hq * w.B * pairs
-
-    def one_step(hook=None, fused_merge=True):
-        kw = {} if hook is None else {"hook": hook}
-        return ring.ring_forward_steps(q, ks, vs, W, True, rank, causal=True,
-                                       fused_merge=fused_merge, **kw)
-
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
-
-    # whole-step timing
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        one_step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    value = flop_per_step / (ms_per_step * 1e-3) / 1e12
-
-    # the same steps timed one by one (median and minimum)
-    per_step = Timer(torch)
-    for _ in range(args.steps):
-        per_step(one_step)
-    per_step.total_ms()
-    step_ms = sorted(a.elapsed_time(b) for a, b in per_step.pairs)
-
-    # per-launch timing of the dominant kernel (the step kernel), on the same stream
-    kern = Timer(torch)
-    merge_t = Timer(torch)
-
-    def hook(kind, fn):
-        return (kern if kind == "step" else merge_t)(fn)
-
-    for _ in range(args.steps):
-        one_step(hook)
-    n_launch = len(kern.pairs)
-    kern_ms = kern.total_ms() / n_launch
-    flop_per_launch = 4 * d * Hq * w.B * pairs / len(plan)
-    achieved = flop_per_launch / (kern_ms * 1e-3) / 1e12
-
-    # the same ring with each merge as its own launch (step kernels write
-    # float32 partials, rattn_merge folds them in)
-    for _ in range(args.warmup):
-        one_step(fused_merge=False)
-    sep_ms = loop_ms(torch, lambda: one_step(fused_merge=False), args.steps)
-    for _ in range(args.steps):
-        one_step(hook, fused_merge=False)
-    merge_ms = merge_t.total_ms() / max(1, len(merge_t.pairs))
-
-    # fused single launch of the same share
-    fo = fl = None
-    for _ in range(args.warmup):
-        fo, fl = binding.fwd(q, k, v, causal=True, n_ring_steps=W, zigzag=True, rank=rank)
-    fused_ms = loop_ms(torch, lambda: binding.fwd(q, k, v, causal=True, n_ring_steps=W,
-                                                  zigzag=True, rank=rank), args.steps)
-    fused_value = flop_per_step / (fused_ms * 1e-3) / 1e12
-
+    if args.ring_share_only:
+        print(json.dumps({"extras": ring_share_extra(torch, binding, ring, workloads, dev, args,
+                                                     None)}), flush=True)
+        return
+    peak = device_peak(torch)
+    w, inputs, flop, pairs, ms_per_step, launch_ms, avg_launch = headline(
+        torch, binding, workloads, dev, args)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (avg_launch * 1e-3) / 1e12
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -452,30 +555,30 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
-        "ms_per_step_min": round(step_ms[0], 4),
+        "ms_per_step_median": round(launch_ms[len(launch_ms) // 2], 4),
+        "ms_per_step_min": round(launch_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: N(0,1) bf16 q/k/v from a seeded torch generator, resident in HBM",
-        "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "N": N, "Hq": Hq, "Hkv": w.Hkv,
-                   "d": d, "causal": True, "ring": W, "zigzag": True, "rank": rank,
-                   "mode": "8 ring-step launches; steps 2-8 merge into the running "
-                           "(out, lse) in the kernel epilogue (LSE merge fused)",
+        "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "N": w.N, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "d": w.d, "causal": True, "ring": w.W, "zigzag": True,
+                   "rank": -1,
+                   "mode": "one rattn_fwd launch per step: the ZigZag ring schedule of all "
+                           "8 simulated devices (16 chunks of 32768 tokens), ring steps merged "
+                           "in place by the online softmax",
                    "visible_pairs_per_head": pairs,
-                   "flop_per_step": flop_per_step,
+                   "flop_per_step": flop,
                    # the usual causal estimate, half of all (query, key) pairs
-                   "conventional_flop_per_step": 4 * d * Hq * w.B * w.Nq * N // 2},
+                   "conventional_flop_per_step": 4 * w.d * w.Hq * w.B * w.Nq * w.N // 2},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": stored_traffic(), "kernel": STEP_KERNEL,
-                     "avg_launch_ms": round(kern_ms, 4), "launches": n_launch},
-        "steps_separate_merge": {"value": round(flop_per_step / (sep_ms * 1e-3) / 1e12, 2),
-                                 "ms": round(sep_ms, 4), "merge_avg_ms": round(merge_ms, 4)},
-        "fused": {"value": round(fused_value, 2), "ms": round(fused_ms, 4),
-                  "pct_of_peak": round(100 * fused_value / PEAK_BF16_TFLOPS, 2)},
+                     "traffic": stored_traffic(HEADLINE_COUNTERS), "kernel": HEADLINE_KERNEL,
+                     "avg_launch_ms": round(avg_launch, 4), "launches": len(launch_ms),
+                     "flop_per_launch": flop},
+        "peak_bf16": peak,
         # context only, not a target: the memory-wall figures of the
         # guijiagi.com ring-attention page (naive attention section) -- a full
         # fp16 score matrix at one million tokens against one GPU's HBM
@@ -485,10 +588,14 @@ def main():
             "page_gpu": "unnamed 80 GB GPU",
             "this_gpu_hbm_bytes": 288 * 10**9,
             "score_matrix_bytes_this_workload_if_materialised":
-                2 * w.B * Hq * w.Nq * N,
+                2 * w.B * w.Hq * w.Nq * w.N,
             "score_bytes_materialised_here": 0},
     }
-    del fo, fl
+    if not args.no_cpu:
+        q, k, v = inputs
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+    del inputs
+    torch.cuda.empty_cache()
 
     if not args.no_extras:
         extras = {}
@@ -502,13 +609,13 @@ def main():
             else:
                 pe = we.Nq * we.N
             fe = 4 * we.d * we.Hq * we.B * pe
-            reps = 3 if idx == 5 else args.steps
-            warm_up(torch, lambda: binding.fwd(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
-                                               zigzag=we.zigzag, rank=we.rank),
-                    1 if idx == 5 else args.warmup, 0.0 if idx == 5 else 0.25)
-            ms = loop_ms(torch, lambda: binding.fwd(qe, ke, ve, causal=we.causal,
-                                                    n_ring_steps=we.W, zigzag=we.zigzag,
-                                                    rank=we.rank), reps)
+            reps = max(20, 2 * args.steps)
+
+            def run():
+                return binding.fwd(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
+                                   zigzag=we.zigzag, rank=we.rank)
+            warm_up(torch, run, 5)
+            ms = loop_ms(torch, run, reps)
             extras[we.name] = {"ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
                                "pct_of_peak": round(100 * fe / (ms * 1e-3) / 1e12
                                                     / PEAK_BF16_TFLOPS, 2)}
@@ -520,7 +627,7 @@ def main():
                 def run_split():
                     return binding.fwd_split(qe, ke, ve, causal=we.causal, n_ring_steps=we.W,
                                              zigzag=we.zigzag, rank=we.rank, n_splits=ns, ws=ws)
-                warm_up(torch, run_split, args.warmup)
+                warm_up(torch, run_split, 5)
                 ms = loop_ms(torch, run_split, reps)
                 extras[we.name + "_splitkv"] = {
                     "ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
@@ -530,19 +637,15 @@ def main():
             del qe, ke, ve
             torch.cuda.empty_cache()
 
-        # the 512K workload runs last: its seconds of full load lower the clock
-        # for whatever follows
+        extras.update(ring_share_extra(torch, binding, ring, workloads, dev, args, peak))
         for idx in (2, 3):
             workload_extra(idx)
+        extras.update(tiny_latency_extra(torch, binding, workloads, dev, args))
         extras.update(small_d_sweep(torch, binding, workloads, dev, args))
         extras.update(backward_extras(torch, binding, ring, workloads, dev, args))
         extras.update(layout_comparison(torch, binding, ring, workloads, dev, args))
         extras.update(varlen_extra(torch, binding, workloads, dev, args))
-        workload_extra(5)
         result["extras"] = extras
-
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
 
     print(json.dumps(result), flush=True)
 
@@ -724,7 +827,8 @@ def cpu_baseline(w, q, k, v, n_rows):
     rows = np.stack([np.zeros(n_rows, np.int64),
                      np.random.default_rng(7).choice(w.Nq, n_rows, replace=False),
                      np.random.default_rng(8).integers(0, w.Hq, n_rows)], axis=1)
-    qpos = layouts.zigzag_shard_positions(w.N, w.W, w.rank)
+    # every device's shard in one call (rank -1): q in natural order
+    qpos = np.arange(w.Nq) if w.rank < 0 else layouts.zigzag_shard_positions(w.N, w.W, w.rank)
     qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
     threads = oracle.default_threads()
     t = time.perf_counter()

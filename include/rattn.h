@@ -82,25 +82,31 @@ RATTN_API int rattn_fwd(const void* q, const void* k, const void* v, void* out, 
  * One ring step: the attention of a set of query rows over one received
  * key/value shard (the per-step block call of the Twinkle forward pass).
  *
- * Query rows [0, q_seg_len[0]) sit at positions q_seg_start[0] + i and rows
- * [q_seg_len[0], Nq) at q_seg_start[1] + (i - q_seg_len[0]); likewise for the
- * Nk key/value rows with k_seg_*.  q_seg_len[0] + q_seg_len[1] == Nq and
- * k_seg_len[0] + k_seg_len[1] == Nk (a length may be 0).  The four segment
- * arrays are HOST pointers to two int64 each.
+ * The step reads query rows [q_off, q_off + Nq) of q [B, q_rows, Hq, d] and
+ * key/value rows [k_off, k_off + Nk) of k_blk, v_blk [B, k_rows, Hkv, d], so
+ * a part of a shard (the back query half, the front key chunk) needs no copy.
+ * Query row q_off + i sits at position q_seg_start[0] + i for
+ * i < q_seg_len[0] and at q_seg_start[1] + (i - q_seg_len[0]) after; likewise
+ * for the Nk key/value rows with k_seg_*.  q_seg_len[0] + q_seg_len[1] == Nq
+ * and k_seg_len[0] + k_seg_len[1] == Nk (a length may be 0); requires
+ * q_off + Nq <= q_rows and k_off + Nk <= k_rows.  The four segment arrays are
+ * HOST pointers to two int64 each.
  * Writes the normalised float32 partial out_part [B, Nq, Hq, d] and
- * lse_part [B, Nq, Hq]; rows that see no key get 0 and -inf, which the merge
- * treats as an empty partial.
+ * lse_part [B, Nq, Hq] (row i for query row q_off + i); rows that see no key
+ * get 0 and -inf, which the merge treats as an empty partial.
  */
 RATTN_API int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk,
                    float* out_part, float* lse_part, int B, int Hq, int Hkv,
-                   int64_t Nq, int64_t Nk, int d, int dtype, float scale, int causal,
+                   int64_t q_rows, int64_t q_off, int64_t Nq, int64_t k_rows, int64_t k_off,
+                   int64_t Nk, int d, int dtype, float scale, int causal,
                    const int64_t* q_seg_start, const int64_t* q_seg_len,
                    const int64_t* k_seg_start, const int64_t* k_seg_len, void* stream);
 
 /*
  * One ring step merged into the running result: rattn_fwd_step's partial for
- * query rows i in [0, Nq) of q, merged by the log-sum-exp correction (Twinkle
- * page, update_out_and_lse; same function as rattn_merge) into
+ * query rows q_off + i, i in [0, Nq), of q, merged by the log-sum-exp
+ * correction (Twinkle page, update_out_and_lse; same function as
+ * rattn_merge) into
  *   (out, lse)[b, row_off + i, h],  out [B, Nq_out, Hq, d] float32,
  *   lse [B, Nq_out, Hq] float32,
  * in the kernel's epilogue (one launch instead of a step and a merge).
@@ -109,11 +115,13 @@ RATTN_API int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk
  * as rattn_fwd_step.
  */
 RATTN_API int rattn_fwd_step_merge(const void* q, const void* k_blk, const void* v_blk,
-                                   float* out, float* lse, int B, int Hq, int Hkv, int64_t Nq,
-                                   int64_t Nk, int d, int dtype, float scale, int causal,
-                                   const int64_t* q_seg_start, const int64_t* q_seg_len,
-                                   const int64_t* k_seg_start, const int64_t* k_seg_len,
-                                   int64_t Nq_out, int64_t row_off, void* stream);
+                                   float* out, float* lse, int B, int Hq, int Hkv,
+                                   int64_t q_rows, int64_t q_off, int64_t Nq, int64_t k_rows,
+                                   int64_t k_off, int64_t Nk, int d, int dtype, float scale,
+                                   int causal, const int64_t* q_seg_start,
+                                   const int64_t* q_seg_len, const int64_t* k_seg_start,
+                                   const int64_t* k_seg_len, int64_t Nq_out, int64_t row_off,
+                                   void* stream);
 
 /*
  * In-place log-sum-exp merge (Twinkle page, update_out_and_lse; computed as

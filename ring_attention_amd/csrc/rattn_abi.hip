@@ -281,16 +281,22 @@ extern "C" int rattn_split_hint(int B, int Hq, int64_t Nq, int64_t N, int d, int
 namespace rattn {
 namespace {
 
-// rattn_fwd_step / rattn_fwd_step_merge: output rows [row_off, row_off + Nq)
-// of a [B, Nq_out, Hq, d] fp32 output; merge = 1 merges into it.
+// rattn_fwd_step / rattn_fwd_step_merge: query rows [q_off, q_off + Nq) of a
+// [B, q_rows, Hq, d] tensor over key/value rows [k_off, k_off + Nk) of
+// [B, k_rows, Hkv, d] tensors; output rows [row_off, row_off + Nq) of a
+// [B, Nq_out, Hq, d] fp32 output; merge = 1 merges into it.
 int fwd_step_impl(const void* q, const void* k_blk, const void* v_blk, float* out,
-                  float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, int d, int dtype,
+                  float* lse, int B, int Hq, int Hkv, int64_t q_rows, int64_t q_off, int64_t Nq,
+                  int64_t k_rows, int64_t k_off, int64_t Nk, int d, int dtype,
                   float scale, int causal, const int64_t* q_seg_start, const int64_t* q_seg_len,
                   const int64_t* k_seg_start, const int64_t* k_seg_len, int64_t Nq_out,
                   int64_t row_off, int merge, void* stream) {
   if (!q_seg_start || !q_seg_len || !k_seg_start || !k_seg_len) return RATTN_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return RATTN_EINVAL;
   if (Nq < 0 || Nk < 0 || row_off < 0 || Nq_out < 0) return RATTN_EINVAL;
+  if (q_off < 0 || k_off < 0 || q_off > q_rows || Nq > q_rows - q_off || k_off > k_rows ||
+      Nk > k_rows - k_off)
+    return RATTN_EINVAL;
   if (row_off > Nq_out || Nq > Nq_out - row_off) return RATTN_EINVAL;
   // a pointer may be null only when its tensor is empty
   if ((Nq > 0 && (!q || !out || !lse)) || (Nk > 0 && (!k_blk || !v_blk))) return RATTN_EINVAL;
@@ -304,7 +310,7 @@ int fwd_step_impl(const void* q, const void* k_blk, const void* v_blk, float* ou
   if (!aligned(q, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) || !aligned(out, 16) ||
       !aligned(lse, 4))
     return RATTN_EINVAL;
-  const int64_t rows_max = std::max(std::max(Nq, Nk), Nq_out);
+  const int64_t rows_max = std::max(std::max(q_rows, k_rows), Nq_out);
   if (!tensor_ok(B, rows_max, Hq > Hkv ? Hq : Hkv, d)) return RATTN_EUNSUPPORTED;
   if (Nq == 0) return RATTN_OK;
 
@@ -315,15 +321,18 @@ int fwd_step_impl(const void* q, const void* k_blk, const void* v_blk, float* ou
   s.W = 1;
   s.causal = causal;
   s.n_kruns = 0;
-  if (k_seg_len[0] > 0) s.kruns[s.n_kruns++] = Run{0, k_seg_len[0], k_seg_start[0]};
-  if (k_seg_len[1] > 0) s.kruns[s.n_kruns++] = Run{k_seg_len[0], k_seg_len[1], k_seg_start[1]};
-  QSeg segs[2] = {QSeg{0, q_seg_len[0], q_seg_start[0], 0, 0},
-                  QSeg{q_seg_len[0], q_seg_len[1], q_seg_start[1], 0, 0}};
+  if (k_seg_len[0] > 0) s.kruns[s.n_kruns++] = Run{k_off, k_seg_len[0], k_seg_start[0]};
+  if (k_seg_len[1] > 0)
+    s.kruns[s.n_kruns++] = Run{k_off + k_seg_len[0], k_seg_len[1], k_seg_start[1]};
+  QSeg segs[2] = {QSeg{q_off, q_seg_len[0], q_seg_start[0], 0, 0},
+                  QSeg{q_off + q_seg_len[0], q_seg_len[1], q_seg_start[1], 0, 0}};
   rc = finalize(s, segs, 2, br);
   if (rc != RATTN_OK) return rc;
-  FwdParams p = make_params(B, Hq, Hkv, Nq, Nk, resolve_scale(scale, d));
+  // rows are addressed in the full [B, q_rows] / [B, k_rows] row spaces; the
+  // kernels write query row r to output row out_row_off + r
+  FwdParams p = make_params(B, Hq, Hkv, q_rows, k_rows, resolve_scale(scale, d));
   p.out_rows = Nq_out;
-  p.out_row_off = row_off;
+  p.out_row_off = row_off - q_off;
   p.merge_out = merge;
   return dispatch(dtype, d, q, k_blk, v_blk, out, lse, true, p, s,
                   (int64_t)s.n_tiles * B * Hq, stream);
@@ -334,24 +343,27 @@ int fwd_step_impl(const void* q, const void* k_blk, const void* v_blk, float* ou
 
 extern "C" int rattn_fwd_step(const void* q, const void* k_blk, const void* v_blk,
                               float* out_part, float* lse_part, int B, int Hq, int Hkv,
-                              int64_t Nq, int64_t Nk, int d, int dtype, float scale, int causal,
-                              const int64_t* q_seg_start, const int64_t* q_seg_len,
+                              int64_t q_rows, int64_t q_off, int64_t Nq, int64_t k_rows,
+                              int64_t k_off, int64_t Nk, int d, int dtype, float scale,
+                              int causal, const int64_t* q_seg_start, const int64_t* q_seg_len,
                               const int64_t* k_seg_start, const int64_t* k_seg_len,
                               void* stream) {
-  return fwd_step_impl(q, k_blk, v_blk, out_part, lse_part, B, Hq, Hkv, Nq, Nk, d, dtype, scale,
-                       causal, q_seg_start, q_seg_len, k_seg_start, k_seg_len, Nq, 0, 0,
-                       stream);
+  return fwd_step_impl(q, k_blk, v_blk, out_part, lse_part, B, Hq, Hkv, q_rows, q_off, Nq,
+                       k_rows, k_off, Nk, d, dtype, scale, causal, q_seg_start, q_seg_len,
+                       k_seg_start, k_seg_len, Nq, 0, 0, stream);
 }
 
 extern "C" int rattn_fwd_step_merge(const void* q, const void* k_blk, const void* v_blk,
-                                    float* out, float* lse, int B, int Hq, int Hkv, int64_t Nq,
-                                    int64_t Nk, int d, int dtype, float scale, int causal,
-                                    const int64_t* q_seg_start, const int64_t* q_seg_len,
-                                    const int64_t* k_seg_start, const int64_t* k_seg_len,
-                                    int64_t Nq_out, int64_t row_off, void* stream) {
-  return fwd_step_impl(q, k_blk, v_blk, out, lse, B, Hq, Hkv, Nq, Nk, d, dtype, scale, causal,
-                       q_seg_start, q_seg_len, k_seg_start, k_seg_len, Nq_out, row_off, 1,
-                       stream);
+                                    float* out, float* lse, int B, int Hq, int Hkv,
+                                    int64_t q_rows, int64_t q_off, int64_t Nq, int64_t k_rows,
+                                    int64_t k_off, int64_t Nk, int d, int dtype, float scale,
+                                    int causal, const int64_t* q_seg_start,
+                                    const int64_t* q_seg_len, const int64_t* k_seg_start,
+                                    const int64_t* k_seg_len, int64_t Nq_out, int64_t row_off,
+                                    void* stream) {
+  return fwd_step_impl(q, k_blk, v_blk, out, lse, B, Hq, Hkv, q_rows, q_off, Nq, k_rows, k_off,
+                       Nk, d, dtype, scale, causal, q_seg_start, q_seg_len, k_seg_start,
+                       k_seg_len, Nq_out, row_off, 1, stream);
 }
 
 extern "C" int rattn_merge(float* out, float* lse, const float* blk_out, const float* blk_lse,

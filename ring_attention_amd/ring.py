@@ -73,35 +73,32 @@ def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag
         src = (rank - s) % W
         k_runs = shard_rows(N, W, zigzag, src)
         kb, vb = k_shards[src], v_shards[src]
-        row_off = 0
-        qv, qr, kr, step_causal = q_shard, q_runs, k_runs, causal
+        row_off = 0  # first query row of the step (rows of the shard are read in place)
+        qr, kr, step_causal = q_runs, k_runs, causal
         if zigzag and causal:
             c = N // (2 * W)
             if s == 0:
                 pass
             elif s <= rank:
-                kb, vb = kb[:, :c], vb[:, :c]
-                kr, step_causal = k_runs[:1], False
+                kr, step_causal = k_runs[:1], False  # the front chunk: key rows [0, c)
             else:
-                qv, qr, row_off, step_causal = q_shard[:, c:], q_runs[1:], c, False
+                qr, row_off, step_causal = q_runs[1:], c, False  # back half: rows [c, 2c)
         elif causal:
             if src > rank:
                 continue
             step_causal = src == rank
-        if not qv.is_contiguous():
-            qv = qv.contiguous()
-        if not kb.is_contiguous():
-            kb, vb = kb.contiguous(), vb.contiguous()
         if out is None:
             # the first step writes the running result directly
-            out, lse = hook("step", lambda: binding.fwd_step(qv, kb, vb, step_causal, qr, kr,
-                                                             scale))
+            out, lse = hook("step", lambda: binding.fwd_step(q_shard, kb, vb, step_causal, qr, kr,
+                                                             scale, q_off=row_off))
             continue
         if fused_merge:
-            hook("step", lambda: binding.fwd_step_merge(qv, kb, vb, step_causal, qr, kr, out, lse,
-                                                        row_off=row_off, scale=scale))
+            hook("step", lambda: binding.fwd_step_merge(q_shard, kb, vb, step_causal, qr, kr, out,
+                                                        lse, row_off=row_off, scale=scale,
+                                                        q_off=row_off))
             continue
-        bo, bl = hook("step", lambda: binding.fwd_step(qv, kb, vb, step_causal, qr, kr, scale))
+        bo, bl = hook("step", lambda: binding.fwd_step(q_shard, kb, vb, step_causal, qr, kr, scale,
+                                                       q_off=row_off))
         hook("merge", lambda: binding.merge(out, lse, bo, bl, row_off=row_off))
     return out, lse
 

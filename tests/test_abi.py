@@ -117,30 +117,37 @@ def seg(a, b):
 
 
 def step(lib, Nq=32, Nk=32, qs=(0, 0), ql=(32, 0), ks=(0, 0), kl=(32, 0), d=128, dtype=1,
-         causal=1, q=P[0], out=P[3], nulls=False):
+         causal=1, q=P[0], out=P[3], nulls=False, q_rows=None, q_off=0, k_rows=None, k_off=0):
     arrs = [None] * 4 if nulls else [seg(*qs), seg(*ql), seg(*ks), seg(*kl)]
-    return lib.rattn_fwd_step(q, P[1], P[2], out, P[4], 1, 4, 2, Nq, Nk, d, dtype, 0.0, causal,
-                              *arrs, None)
+    q_rows = Nq if q_rows is None else q_rows
+    k_rows = Nk if k_rows is None else k_rows
+    return lib.rattn_fwd_step(q, P[1], P[2], out, P[4], 1, 4, 2, q_rows, q_off, Nq, k_rows,
+                              k_off, Nk, d, dtype, 0.0, causal, *arrs, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(nulls=True), EINVAL), (dict(q=0), EINVAL), (dict(ql=(30, 0)), EINVAL),
     (dict(kl=(16, 8)), EINVAL), (dict(ql=(40, -8)), EINVAL), (dict(d=12), EUNSUP),
     (dict(dtype=-1), EINVAL), (dict(causal=-1), EINVAL), (dict(out=P[3] + 4), EINVAL),
+    # row ranges outside the query / key row spaces
+    (dict(q_off=1), EINVAL), (dict(q_off=-1, q_rows=64), EINVAL), (dict(q_rows=31), EINVAL),
+    (dict(k_off=40, k_rows=64), EINVAL), (dict(k_off=-1, k_rows=64), EINVAL),
 ])
 def test_fwd_step_rejects(rattn_lib, kw, status):
     assert step(rattn_lib, **kw) == status
 
 
-def step_merge(lib, Nq=32, Nq_out=64, off=0, q=P[0], out=P[3]):
-    return lib.rattn_fwd_step_merge(q, P[1], P[2], out, P[4], 1, 4, 2, Nq, 32, 128, 1, 0.0, 1,
-                                    seg(0, 0), seg(Nq, 0), seg(0, 0), seg(32, 0), Nq_out, off,
-                                    None)
+def step_merge(lib, Nq=32, Nq_out=64, off=0, q=P[0], out=P[3], q_rows=None, q_off=0):
+    q_rows = Nq if q_rows is None else q_rows
+    return lib.rattn_fwd_step_merge(q, P[1], P[2], out, P[4], 1, 4, 2, q_rows, q_off, Nq, 32, 0,
+                                    32, 128, 1, 0.0, 1, seg(0, 0), seg(Nq, 0), seg(0, 0),
+                                    seg(32, 0), Nq_out, off, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(off=40), EINVAL), (dict(off=-1), EINVAL), (dict(Nq_out=16), EINVAL),
     (dict(Nq_out=-1), EINVAL), (dict(q=0), EINVAL), (dict(out=P[3] + 4), EINVAL),
+    (dict(q_off=8, q_rows=32), EINVAL),
 ])
 def test_fwd_step_merge_rejects(rattn_lib, kw, status):
     assert step_merge(rattn_lib, **kw) == status

@@ -285,6 +285,57 @@ def test_ring_steps_equal_oracle(gpu, W, zigzag, fused_merge):
                 what=f"steps W={W} zigzag={zigzag} rank={r}")
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64),
+                                     (torch.float32, 32)])
+@pytest.mark.parametrize("fused_merge", [True, False])
+def test_ring_steps_batched_read_shards_in_place(gpu, dtype, d, fused_merge):
+    """B = 2: the ZigZag ring steps read the back query half and the front key
+    chunk of each shard through row offsets (no per-step copies); every
+    device's result against the oracle, and the shards are left untouched."""
+    W, N = 4, 2 * 4 * 72  # chunks of 72 rows: ragged tiles on every kernel
+    q, k, v = workloads.make_qkv(2, N, N, 4, 2, d, dtype, seed=70 + d)
+    dev = torch.device("cuda:0")
+    kd, vd = k.to(dev), v.to(dev)
+    ks = [ring.shard(kd, W, True, r) for r in range(W)]
+    vs = [ring.shard(vd, W, True, r) for r in range(W)]
+    ks_before = [x.clone() for x in ks]
+    for r in range(W):
+        qs = ring.shard(q, W, True, r)
+        qd = qs.to(dev)
+        out, lse = ring.ring_forward_steps(qd, ks, vs, W, True, r, fused_merge=fused_merge)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.attention(qs, k, v, causal=True,
+                                        q_pos=layouts.shard_positions(N, W, r, True))
+        compare(host(out), host(lse), ref_o, ref_l, dtype,
+                what=f"B=2 steps {dtype} d={d} rank={r} fused={fused_merge}")
+        assert torch.equal(qd, qs.to(dev))
+    assert all(torch.equal(a, b) for a, b in zip(ks, ks_before))
+
+
+def test_step_row_offsets_match_copies(gpu):
+    """rattn_fwd_step on rows [q_off, q_off + Nq) x [k_off, k_off + Nk) of
+    larger tensors equals the same step on copies of those rows, bit for bit
+    (B = 3, GQA, d = 128 and d = 64)."""
+    dev = torch.device("cuda:0")
+    for d in (128, 64):
+        q, k, v = workloads.make_qkv(3, 700, 900, 4, 2, d, torch.bfloat16, seed=80 + d,
+                                     device=dev)
+        q_off, Nq, k_off, Nk = 133, 400, 257, 520
+        q_segs, k_segs = [(1000, 150), (5000, 250)], [(900, 300), (4800, 220)]
+        a_o, a_l = binding.fwd_step(q, k, v, True, q_segs, k_segs, q_off=q_off, k_off=k_off)
+        b_o, b_l = binding.fwd_step(q[:, q_off:q_off + Nq].contiguous(),
+                                    k[:, k_off:k_off + Nk].contiguous(),
+                                    v[:, k_off:k_off + Nk].contiguous(), True, q_segs, k_segs)
+        torch.cuda.synchronize()
+        assert torch.equal(a_o, b_o) and torch.equal(a_l, b_l), d
+        ref_o, ref_l = oracle.attention(
+            q[:, q_off:q_off + Nq].cpu(), k[:, k_off:k_off + Nk].cpu(),
+            v[:, k_off:k_off + Nk].cpu(), causal=True,
+            q_pos=np.concatenate([np.arange(1000, 1150), np.arange(5000, 5250)]),
+            k_pos=np.concatenate([np.arange(900, 1200), np.arange(4800, 5020)]))
+        compare(host(a_o), host(a_l), ref_o, ref_l, torch.bfloat16, what=f"offsets d={d}")
+
+
 def test_noncausal_result_independent_of_schedule(gpu):
     q, k, v = workloads.make_qkv(1, 512, 512, 2, 2, 128, torch.float16, seed=3, device=gpu)
     base, base_l = binding.fwd(q, k, v)
