@@ -83,10 +83,6 @@ def parse():
                          "and print its JSON")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a summary of a rocprofv3 --stats kernel_stats.csv and exit")
-    ap.add_argument("--summarize-step-dispatches", metavar="KERNEL_TRACE_CSV",
-                    help="print the ring-step kernel's mean duration over the dispatches of "
-                         "the timed per-launch pass (from a rocprofv3 --kernel-trace csv of a "
-                         "default run with the same --steps/--warmup) and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, then WRITE_SIZE; counter_collection.csv) and exit")
@@ -122,23 +118,6 @@ def summarize_stats(path: str) -> None:
         print(f"{_short_name(r['Name'])[:60]:60s} {int(r['Calls']):6d} "
               f"{float(r['AverageNs']) / 1e3:10.1f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
               f"{float(r['Percentage']):6.2f}")
-
-
-def summarize_step_dispatches(path: str, args) -> None:
-    """The step kernel's dispatches in trace order: per ring step 8 launches;
-    warmup, the timed steps, the per-step timing pass, then the per-launch
-    pass whose HIP-event average bench.py reports (roofline.avg_launch_ms)."""
-    import csv
-    rows = [r for r in csv.DictReader(open(path)) if _short_name(r["Kernel_Name"]) == STEP_KERNEL]
-    us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
-    a = 8 * (args.warmup + 2 * args.steps)
-    b = a + 8 * args.steps
-    seg = us[a:b]
-    print(f"kernel: {STEP_KERNEL}")
-    print(f"dispatches_in_trace: {len(us)}")
-    print(f"per_launch_pass_dispatches: [{a}, {b})")
-    print(f"per_launch_pass_avg_us: {sum(seg) / max(1, len(seg)):.1f}")
-    print(f"all_dispatches_avg_us: {sum(us) / max(1, len(us)):.1f}  (includes the extras)")
 
 
 def _counter_means(path: str, counter: str):
@@ -499,9 +478,6 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.kernel or HEADLINE_KERNEL)
-        return
-    if args.summarize_step_dispatches:
-        summarize_step_dispatches(args.summarize_step_dispatches, args)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, args.kernel or HEADLINE_KERNEL)
