@@ -52,7 +52,8 @@ typedef enum {
   RATTN_OK = 0,
   RATTN_EINVAL = -1,       /* invalid argument (null pointer, bad size, ...) */
   RATTN_EUNSUPPORTED = -2, /* valid but not implemented (d, dtype, W > 32) */
-  RATTN_EHIP = -3          /* HIP reported an error when enqueueing */
+  RATTN_EHIP = -3,         /* HIP reported an error when enqueueing */
+  RATTN_ESCRATCH = -4      /* larger than the library's fixed scratch (rattn_fwd_split_noalloc) */
 } rattn_status;
 
 typedef enum { RATTN_F32 = 0, RATTN_F16 = 1, RATTN_BF16 = 2 } rattn_dtype;
@@ -180,6 +181,33 @@ RATTN_API int rattn_fwd_split(const void* q, const void* k, const void* v, void*
                               int dtype, float scale, int causal, int n_ring_steps, int zigzag,
                               int rank, int n_splits, float* ws, int64_t ws_floats,
                               void* stream);
+
+/*
+ * rattn_fwd_split for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and result, with the split partials in a scratch
+ * array the library owns instead of caller workspace.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - The scratch is a fixed array of RATTN_NOALLOC_SCRATCH_FLOATS float32
+ *     (32 MiB) per GPU, resolved on the first call on that GPU and held until
+ *     the process ends.  A call needs n_splits * B * Nq * Hq * (d + 1) floats
+ *     when n_splits > 1; larger calls return RATTN_ESCRATCH and enqueue
+ *     nothing.  n_splits = 1 is rattn_fwd and uses no scratch.
+ *   - Every call on one GPU shares that GPU's array and leaves the last
+ *     call's partials in it (nothing in it needs to start at zero: each call
+ *     writes every entry it reads).  Calls that may overlap on one GPU (on
+ *     different streams without ordering between them) race; order them on
+ *     one stream.
+ *   - The GPU is the current device of the calling thread, which must be
+ *     the device of `stream`.
+ * Other arguments and errors as rattn_fwd_split (no ws, ws_floats).
+ */
+#define RATTN_NOALLOC_SCRATCH_FLOATS (8LL << 20)
+RATTN_API int rattn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* out,
+                                      float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t N,
+                                      int d, int dtype, float scale, int causal,
+                                      int n_ring_steps, int zigzag, int rank, int n_splits,
+                                      void* stream);
 
 /*
  * A split count for rattn_fwd_split: 1 when the query tiles alone give at

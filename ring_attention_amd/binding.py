@@ -20,7 +20,8 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # Exported symbols, in the order include/rattn.h declares them.
 EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_fwd_step_merge", "rattn_merge",
-           "rattn_fwd_varlen", "rattn_fwd_split", "rattn_split_hint", "rattn_bwd_delta",
+           "rattn_fwd_varlen", "rattn_fwd_split", "rattn_fwd_split_noalloc",
+           "rattn_split_hint", "rattn_bwd_delta",
            "rattn_bwd", "rattn_bwd_varlen", "rattn_bwd_step", "rattn_status_string")
 
 
@@ -68,6 +69,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rattn_fwd_split.restype = i32
     lib.rattn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
                                     i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.rattn_fwd_split_noalloc.restype = i32
+    lib.rattn_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32,
+                                            f32, i32, i32, i32, i32, i32, vp]
     lib.rattn_split_hint.restype = i32
     lib.rattn_split_hint.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32]
     lib.rattn_bwd_delta.restype = i32
@@ -183,6 +187,30 @@ def fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
                              int(bool(zigzag)), int(rank), int(n_splits), ws.data_ptr(),
                              ws.numel(), _stream(q))
     _check("rattn_fwd_split", rc)
+    return out, lse
+
+
+def fwd_split_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                      n_ring_steps: int = 1, zigzag: bool = False, rank: int = -1,
+                      scale: float | None = None, n_splits: int | None = None,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """rattn_fwd_split with the library's fixed scratch for the partials
+    (rattn_fwd_split_noalloc: the C call allocates nothing; calls that overlap
+    on one GPU race).  n_splits=None takes rattn_split_hint's count."""
+    _qkv(q, k, v)
+    B, Nq, Hq, d = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    if n_splits is None:
+        n_splits = split_hint(q, k, n_ring_steps, zigzag, rank)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    rc = load_library().rattn_fwd_split_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+        Nq, N, d, DTYPE_CODES[q.dtype], _scale(scale), int(bool(causal)), int(n_ring_steps),
+        int(bool(zigzag)), int(rank), int(n_splits), _stream(q))
+    _check("rattn_fwd_split_noalloc", rc)
     return out, lse
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "bwd.h"
 #include "launch.h"
@@ -256,6 +257,65 @@ extern "C" int rattn_fwd_split(const void* q, const void* k, const void* v, void
   const hipError_t e = launch_split_reduce(dtype, d, out, lse, ws_out, ws_lse, n_splits, rows,
                                            (hipStream_t)stream);
   return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+}
+
+// ---- split-KV without allocation -------------------------------------------
+
+// The partials of rattn_fwd_split_noalloc: one fixed array per GPU (each GPU
+// that runs the library holds its own copy).  Host code never passes this
+// name to a kernel: on the host it is a stand-in, not a device address; the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[RATTN_NOALLOC_SCRATCH_FLOATS];
+
+namespace rattn {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The scratch of the calling thread's current device.
+int device_scratch(float** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return RATTN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return RATTN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RATTN_EHIP;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RATTN_OK;
+}
+
+}  // namespace
+}  // namespace rattn
+
+extern "C" int rattn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, int B, int Hq, int Hkv, int64_t Nq,
+                                       int64_t N, int d, int dtype, float scale, int causal,
+                                       int n_ring_steps, int zigzag, int rank, int n_splits,
+                                       void* stream) {
+  if (n_splits < 1) return RATTN_EINVAL;
+  if (n_splits > kMaxSplits) return RATTN_EUNSUPPORTED;
+  Sched s;
+  const int rc = prepare_ring(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, causal,
+                              n_ring_steps, zigzag, rank, &s);
+  if (rc != RATTN_OK || Nq == 0) return rc;
+  if (n_splits == 1)
+    return rattn_fwd(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, scale, causal,
+                     n_ring_steps, zigzag, rank, stream);
+  int64_t need;
+  if (!mul_ok((int64_t)B * Nq * Hq, (int64_t)d + 1, &need) || !mul_ok(need, n_splits, &need) ||
+      need > RATTN_NOALLOC_SCRATCH_FLOATS)
+    return RATTN_ESCRATCH;
+  float* ws = nullptr;
+  const int sc = device_scratch(&ws);
+  if (sc != RATTN_OK) return sc;
+  return rattn_fwd_split(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, scale, causal,
+                         n_ring_steps, zigzag, rank, n_splits, ws, RATTN_NOALLOC_SCRATCH_FLOATS,
+                         stream);
 }
 
 extern "C" int rattn_split_hint(int B, int Hq, int64_t Nq, int64_t N, int d, int dtype,
@@ -590,6 +650,7 @@ extern "C" const char* rattn_status_string(int status) {
     case RATTN_EINVAL: return "invalid argument";
     case RATTN_EUNSUPPORTED: return "unsupported configuration";
     case RATTN_EHIP: return "HIP error while enqueueing work";
+    case RATTN_ESCRATCH: return "larger than the library's fixed scratch";
     default: return "unknown status";
   }
 }

@@ -100,6 +100,48 @@ def test_fwd_split_empty_is_ok_without_launch(rattn_lib):
     assert fwd_split(rattn_lib, N=0, Nq=0, ws=0) == OK
 
 
+def split_noalloc(lib, n_splits=4, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4], B=1, Hq=2, Hkv=2, Nq=64, N=64, d=64,
+             dtype=2, scale=0.0, causal=1, W=1, zigzag=0, rank=-1)
+    a.update(kw)
+    return lib.rattn_fwd_split_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                       a["Hq"], a["Hkv"], a["Nq"], a["N"], a["d"], a["dtype"],
+                                       a["scale"], a["causal"], a["W"], a["zigzag"], a["rank"],
+                                       n_splits, None)
+
+
+ESCRATCH = -4
+SCRATCH_FLOATS = 8 << 20  # RATTN_NOALLOC_SCRATCH_FLOATS
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_splits=0), EINVAL), (dict(n_splits=65), EUNSUP), (dict(q=0), EINVAL),
+    (dict(Hq=3), EINVAL), (dict(d=48), EUNSUP), (dict(out=P[3] + 4), EINVAL),
+    # partials beyond the fixed scratch: 64 * 1 * 65536 * 2 * 129 floats > 8M
+    (dict(n_splits=64, Nq=65536, N=65536), ESCRATCH),
+    (dict(n_splits=2, B=1, Hq=32, Hkv=8, Nq=1024, N=1024, d=128), ESCRATCH),
+])
+def test_fwd_split_noalloc_rejects(rattn_lib, kw, status):
+    """Argument checks, and calls whose partials exceed the library's fixed
+    scratch, are refused on the host before any device work."""
+    assert split_noalloc(rattn_lib, **kw) == status
+
+
+def test_fwd_split_noalloc_scratch_bound(rattn_lib):
+    def need(n, B, Nq, Hq, d):
+        return n * B * Nq * Hq * (d + 1)
+    assert need(2, 1, 1024, 32, 128) > SCRATCH_FLOATS          # the last case above
+    assert need(8, 1, 4096, 1, 128) <= SCRATCH_FLOATS          # one 4096-row head, 8 splits
+    assert b"scratch" in rattn_lib.rattn_status_string(ESCRATCH)
+
+
+def test_fwd_split_noalloc_empty_and_single_split_need_no_scratch(rattn_lib):
+    assert split_noalloc(rattn_lib, N=0, Nq=0) == OK
+    # a single split is rattn_fwd: no scratch, any size (here: fails only to launch)
+    rc = split_noalloc(rattn_lib, n_splits=1, Nq=65536, N=65536)
+    assert rc in (OK, EHIP)
+
+
 def test_split_hint(rattn_lib):
     h = rattn_lib.rattn_split_hint
     # (B, Hq, Nq, N, d, dtype, W, zigzag, rank, n_cu)
