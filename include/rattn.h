@@ -22,6 +22,8 @@
  *     after the query's (youngju.dev "Ring Attention" analysis, causal step).
  *   - scale <= 0 (or NaN) selects 1/sqrt(d).
  *   - d must be one of 16, 32, 64, 128.
+ *   - Every sequence length (Nq, Nk, N, and each varlen sequence) is below
+ *     2^31 rows; larger sizes return RATTN_EUNSUPPORTED.
  *   - Every pointer argument that names a tensor is a DEVICE pointer owned by
  *     the caller; it may be NULL only when that tensor has no rows.  The library allocates no memory, keeps no global state and
  *     never synchronises the host: work is enqueued on `stream` (a

@@ -51,14 +51,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
+// Direct-to-LDS DMA (LDS address in M0).  Each asm block begins with 5 wait
+// states: the compiler does not look inside inline asm for hazards, and on
+// gfx950 a VMEM instruction that reads an SGPR (M0, the resource, the scalar
+// offset) written by a VALU instruction must follow it by at least 5.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
@@ -78,7 +82,7 @@ __device__ __forceinline__ v4i tensor_rsrc(const void* base) {
 }
 // soff: the wave-uniform part of the offset (scalar), voff: the lane part
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t soff, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))

@@ -74,8 +74,13 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 // resource plus a 32-bit lane offset (buffer_load_dwordx4 ... lds).  The
 // buffer form, with one resource per key/value head, measured 2.5% faster on
 // the ring share; it is used when a head's rows span less than 4 GB.
+// Each asm block begins with 5 wait states: the compiler does not look
+// inside inline asm for hazards, and on gfx950 a VMEM instruction that reads
+// an SGPR (M0, the resource, the scalar offset) written by a VALU instruction
+// (v_readfirstlane, or v_readlane when the compiler restores a spilled SGPR)
+// must follow it by at least 5 wait states.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
@@ -91,10 +96,12 @@ __device__ __forceinline__ v4i head_rsrc(const char* base) {
   r[3] = 0x00020000;
   return r;
 }
-__device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+// soff: the tile's byte offset (wave-uniform, scalar), voff: the lane's part
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t soff, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -111,6 +118,86 @@ __device__ __forceinline__ v4s read_tr(const char* lds, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4s*)(
           (__attribute__((address_space(3))) char*)(lds + off)));
+}
+
+// Cursor over the live key tiles of one query tile in ring order, with what
+// the tile loop needs of the current run computed once per run, so that the
+// per-tile tests are 32-bit scalar compares: a run holds fewer than 2^31 rows
+// (the host rejects larger tensors), so its tile counts fit in 32 bits.
+struct RunCursor {
+  int32_t v, nv;     // visit (run) index, number of visits
+  int32_t t, nt;     // tile within the run, live tiles of the run
+  int32_t n_full;    // tiles of the run that hold BC rows
+  int32_t t_live;    // this wave: tiles t < t_live hold a key visible to one of its rows
+  int32_t t_nomask;  // this wave: tiles t < t_nomask are full and visible to all its rows
+  int64_t row0, pos0, len;
+};
+
+struct RunCursorCtx {
+  const Sched* s;
+  int32_t rank;
+  int64_t qhi;                // last query position of the work item
+  int64_t wave_qlo, wave_qhi; // this wave's first and last query positions
+  bool wave_active;
+};
+
+__device__ __forceinline__ int32_t clamp_tiles(int64_t x, int32_t hi) {
+  return x < 0 ? 0 : (x > hi ? hi : (int32_t)x);
+}
+
+__device__ __forceinline__ void run_load(RunCursor& c, const RunCursorCtx& x) {
+  const Run r = visit(*x.s, x.rank, c.v);
+  c.row0 = r.row0;
+  c.pos0 = r.pos0;
+  c.len = r.len;
+  c.nt = (int32_t)live_tiles(r, x.qhi, x.s->causal, BC);
+  c.n_full = clamp_tiles(r.len / BC, c.nt);
+  if (!x.wave_active) {
+    c.t_live = c.t_nomask = 0;
+  } else if (x.s->causal) {
+    // floor division by BC of possibly negative positions: arithmetic shift
+    c.t_live = clamp_tiles(((x.wave_qhi - r.pos0) >> 6) + 1, c.nt);
+    c.t_nomask = clamp_tiles(((x.wave_qlo - r.pos0 - (BC - 1)) >> 6) + 1, c.n_full);
+  } else {
+    c.t_live = c.nt;
+    c.t_nomask = c.n_full;
+  }
+  c.t = 0;
+}
+
+__device__ __forceinline__ void run_settle(RunCursor& c, const RunCursorCtx& x) {
+  while (c.t >= c.nt) {
+    ++c.v;
+    if (c.v >= c.nv) return;
+    run_load(c, x);
+  }
+}
+
+// Cursor on live tile number t0 of the work item (0-based), or past the end.
+__device__ __forceinline__ RunCursor run_cursor_at(const RunCursorCtx& x, int64_t t0) {
+  RunCursor c;
+  c.nv = num_visits(*x.s);
+  c.v = 0;
+  c.t = 0;
+  c.nt = 0;
+  c.row0 = c.pos0 = c.len = 0;
+  c.n_full = c.t_live = c.t_nomask = 0;
+  if (c.nv > 0) {
+    run_load(c, x);
+    run_settle(c, x);
+  }
+  while (c.v < c.nv && t0 >= c.nt - c.t) {
+    t0 -= c.nt - c.t;
+    c.t = c.nt;
+    run_settle(c, x);
+  }
+  if (c.v < c.nv) c.t += (int32_t)t0;
+  return c;
+}
+
+__device__ __forceinline__ void run_next(RunCursor& c, const RunCursorCtx& x) {
+  ++c.t;
+  if (c.t >= c.nt) run_settle(c, x);
 }
 
 template <typename TT, bool OUT_F32, bool BUF>
@@ -187,34 +274,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   // block 2w+i, part 2i+1 is V block 2w+i.
   // BUF: the head's K and V rows as buffer resources, built once
   const v4i krs = BUF ? head_rsrc(kbase) : v4i{}, vrs = BUF ? head_rsrc(vbase) : v4i{};
+  // One tile's request: its first row, whether it holds BC rows (else the
+  // rows of the run from krow0 on) and its LDS buffer.  Lane offsets are the
+  // precomputed kdma_off / vdma_off, except in the ragged last tile of a run,
+  // whose rows past the end repeat the last row (finite values; their scores
+  // are masked, so p = 0 for them).
   struct DmaPlan {
-    const char* src[4];  // lane addresses (global form)
-    uint32_t off[4];     // lane offsets into krs / vrs (buffer form)
-    uint32_t dst[4];
+    int64_t krow0;
+    int rem;       // rows from krow0 on, at most BC
+    bool full;
+    uint32_t lds;  // LDS address of the K half of the buffer
     bool on;
   };
-  auto plan_tile = [&](const TileCursor& c, int buf) {
+  auto plan_tile = [&](const RunCursor& c, int buf) {
     DmaPlan dp;
-    const int64_t krow0 = c.run.row0 + c.t * BC;
-    const int64_t rem = c.run.len - c.t * BC;
-    const char* kt = kbase + krow0 * (int64_t)row_bytes;
-    const char* vt = vbase + krow0 * (int64_t)row_bytes;
-    const uint32_t t_off = (uint32_t)(krow0 * (int64_t)row_bytes);
-    const uint32_t lk = smem_addr + buf * kBufBytes;
-    const uint32_t lv = lk + kTileBytes;
-    // ragged last tile of a run: rows past its end repeat the last row
-    // (finite values; their scores are masked, so p = 0 for them)
-    const int last = rem < BC ? (int)rem - 1 : BC - 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t back = dma_row[i] > last ? (uint32_t)(dma_row[i] - last) * row_bytes : 0u;
-      dp.src[2 * i] = kt + (kdma_off[i] - back);
-      dp.src[2 * i + 1] = vt + (vdma_off[i] - back);
-      dp.off[2 * i] = t_off + (kdma_off[i] - back);
-      dp.off[2 * i + 1] = t_off + (vdma_off[i] - back);
-      dp.dst[2 * i] = lk + (2 * wave + i) * 1024;
-      dp.dst[2 * i + 1] = lv + (2 * wave + i) * 1024;
-    }
+    dp.krow0 = c.row0 + (int64_t)c.t * BC;
+    dp.full = c.t < c.n_full;
+    dp.rem = dp.full ? BC : (int)(c.len - (int64_t)c.t * BC);
+    dp.lds = smem_addr + buf * kBufBytes;
     dp.on = true;
     return dp;
   };
@@ -237,10 +314,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   }
 
   // ---- tile bookkeeping ----------------------------------------------------
-  int64_t n_tiles;  // key tiles of this work item (of its split)
-  TileCursor cdma = split_cursor<BC>(s, qt.rank, qhi, wi.split, p.n_splits, &n_tiles);
-  const int T = (int)n_tiles;
-  TileCursor cqk = cdma;  // next tile this group scores; cdma: next tile to request
+  int T;  // key tiles of this work item (of its split)
+  const RunCursorCtx cx{&s, qt.rank, qhi, wave_qlo, wave_qhi, wave_active};
+  RunCursor cdma;
+  {
+    // split s of n takes tiles [T s / n, T (s+1) / n) of the T live tiles
+    const int64_t all = count_live_tiles<BC>(s, qt.rank, qhi);
+    const int64_t b0 = all * wi.split / p.n_splits, b1 = all * (wi.split + 1) / p.n_splits;
+    T = (int)(b1 - b0);
+    cdma = run_cursor_at(cx, b0);
+  }
+  RunCursor cqk = cdma;  // next tile this group scores; cdma: next tile to request
   int n_req = 0;
   // plan the next tile's DMA (none once all T tiles are requested)
   auto plan_next = [&]() {
@@ -248,19 +332,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
     dp.on = false;
     if (n_req < T) {
       dp = plan_tile(cdma, n_req & (kNBuf - 1));
-      cursor_next<BC>(cdma, s, qt.rank, qhi);
+      run_next(cdma, cx);
       ++n_req;
     }
     return dp;
   };
   auto issue_all = [&](const DmaPlan& dp) {
-    if (dp.on) {
+    if (!dp.on) return;
+    if (BUF && dp.full) {
+      // full tile: its byte offset in the scalar soffset, lane offsets as
+      // precomputed (no per-tile vector work)
+      const uint32_t t_off = (uint32_t)(dp.krow0 * (int64_t)row_bytes);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (BUF)
-          dma16((q & 1) ? vrs : krs, dp.off[q], dp.dst[q]);
-        else
-          dma16(dp.src[q], dp.dst[q]);
+      for (int i = 0; i < 2; ++i) {
+        dma16(krs, t_off, kdma_off[i], dp.lds + (2 * wave + i) * 1024);
+        dma16(vrs, t_off, vdma_off[i], dp.lds + kTileBytes + (2 * wave + i) * 1024);
+      }
+      return;
+    }
+    const int last = dp.rem - 1;
+    const int64_t tb = dp.krow0 * (int64_t)row_bytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t back = dma_row[i] > last ? (uint32_t)(dma_row[i] - last) * row_bytes : 0u;
+      const uint32_t lk = dp.lds + (2 * wave + i) * 1024;
+      if (BUF) {
+        dma16(krs, (uint32_t)tb, kdma_off[i] - back, lk);
+        dma16(vrs, (uint32_t)tb, vdma_off[i] - back, lk + kTileBytes);
+      } else {
+        dma16(kbase + tb + (kdma_off[i] - back), lk);
+        dma16(vbase + tb + (vdma_off[i] - back), lk + kTileBytes);
       }
     }
   };
@@ -352,16 +453,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   // The scalar bookkeeping (tile positions, cursor) runs here too, where it
   // issues between the VALU work instead of delaying the matrix stream.
   auto v_phase = [&]() {
-    s_kpos0 = cqk.run.pos0 + cqk.t * BC;
-    const int64_t rem = cqk.run.len - cqk.t * BC;
-    s_krows = rem < BC ? (int)rem : BC;
-    const bool s_live = wave_active && (!s.causal || s_kpos0 <= wave_qhi);
-    cursor_next<BC>(cqk, s, qt.rank, qhi);
+    const int32_t t = cqk.t;
+    const bool s_live = t < cqk.t_live;
+    const bool need_mask = t >= cqk.t_nomask;
+    s_kpos0 = cqk.pos0 + (int64_t)t * BC;
+    s_krows = t < cqk.n_full ? BC : (int)(cqk.len - (int64_t)t * BC);
+    run_next(cqk, cx);
     if (!s_live) {
       pk = f32x16{};  // P = 0
       return;
     }
-    const bool need_mask = s_krows < BC || (s.causal && s_kpos0 + s_krows - 1 > wave_qlo);
     bool sees_key = true;  // this lane's query has a visible key in the tile
     if (need_mask) {
       // key index of register r of block kb is kb*32 + 8(r/4) + 4hl + r%4;

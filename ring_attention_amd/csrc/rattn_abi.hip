@@ -28,10 +28,12 @@ bool mul_ok(int64_t a, int64_t b, int64_t* r) {
   return true;
 }
 
-// Element count of a [B, N, H, d] tensor fits comfortably in 64-bit offsets.
+// Element count of a [B, N, H, d] tensor fits comfortably in 64-bit offsets,
+// and N rows in 31 bits (the kernels count rows and tiles of a run in 32 bits).
 bool tensor_ok(int64_t B, int64_t N, int64_t H, int64_t d) {
   int64_t x;
-  return mul_ok(B, N, &x) && mul_ok(x, H, &x) && mul_ok(x, d, &x) && x < ((int64_t)1 << 60);
+  return N < ((int64_t)1 << 31) && mul_ok(B, N, &x) && mul_ok(x, H, &x) && mul_ok(x, d, &x) &&
+         x < ((int64_t)1 << 60);
 }
 
 // Fill tile_begin in longest-first order (causal: the segment with the latest

@@ -62,6 +62,8 @@ def fwd(lib, q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4], B=1, Hq=2, Hkv=2, Nq=64
     (dict(q=P[0] + 2), EINVAL), (dict(out=P[3] + 8), EINVAL), (dict(lse=P[4] + 2), EINVAL),
     (dict(N=-4, Nq=-4), EINVAL), (dict(B=1 << 30, Hq=1 << 30, Hkv=1 << 30, N=1 << 20,
                                        Nq=1 << 20, d=128), EUNSUP),
+    # a sequence of 2^31 rows (the kernels count a run's rows in 32 bits)
+    (dict(B=1, Hq=1, Hkv=1, N=1 << 31, Nq=1 << 31), EUNSUP),
 ])
 def test_fwd_rejects(rattn_lib, kw, status):
     assert fwd(rattn_lib, **kw) == status
