@@ -14,6 +14,7 @@
 // the unrounded p.  This kernel carries the float32 path; the MFMA kernels
 // carry every 16-bit case (the 16-bit branches here are kept for completeness).
 #include "kcommon.h"
+#include "launch.h"
 
 namespace rattn {
 
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(64) void fwd_generic_kernel(
   const int32_t bh = wi.bh;
   const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
-  const QTile qt = query_tile(s, t_lin);
+  const QTile qt = query_tile(s, t_lin, kGenericBr);
   if (qt.rows <= 0) return;  // varlen: a tile past the end of its sequence
 
   const bool q_valid = lane < qt.rows;

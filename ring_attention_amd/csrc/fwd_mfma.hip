@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
   const int32_t bh = xcd_head_swizzle(wi.bh, BH);
   const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
-  const QTile qt = query_tile(s, t_lin);
+  const QTile qt = query_tile(s, t_lin, kMfmaBr);
   if (qt.rows <= 0) return;  // varlen: a tile past the end of its sequence
   const int64_t qhi = qt.pos0 + qt.rows - 1;
 

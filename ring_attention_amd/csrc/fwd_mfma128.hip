@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   const int32_t bh = xcd_head_swizzle(wi.bh, BH);
   const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
-  const QTile qt = query_tile(s, t_lin);
+  const QTile qt = query_tile(s, t_lin, kBr);
   if (qt.rows <= 0) return;  // varlen: a tile past the end of its sequence
   const int64_t qhi = qt.pos0 + qt.rows - 1;
 
@@ -320,7 +320,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   {
     // split s of n takes tiles [T s / n, T (s+1) / n) of the T live tiles
     const int64_t all = count_live_tiles<BC>(s, qt.rank, qhi);
-    const int64_t b0 = all * wi.split / p.n_splits, b1 = all * (wi.split + 1) / p.n_splits;
+    int64_t b0 = 0, b1 = all;
+    if (p.n_splits > 1) {  // the 64-bit divisions run in software: only when split
+      b0 = all * wi.split / p.n_splits;
+      b1 = all * (wi.split + 1) / p.n_splits;
+    }
     T = (int)(b1 - b0);
     cdma = run_cursor_at(cx, b0);
   }

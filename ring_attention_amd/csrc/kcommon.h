@@ -197,6 +197,10 @@ __device__ __forceinline__ TileCursor split_cursor(const Sched& s, int32_t rank,
                                                    int32_t split, int32_t n_splits,
                                                    int64_t* count) {
   const int64_t T = count_live_tiles<BC>(s, rank, qhi);
+  if (n_splits == 1) {  // no split: skip the (software) 64-bit divisions
+    *count = T;
+    return cursor_begin<BC>(s, rank, qhi);
+  }
   const int64_t b0 = T * split / n_splits, b1 = T * (split + 1) / n_splits;
   *count = b1 - b0;
   return cursor_at<BC>(s, rank, qhi, b0);

@@ -96,6 +96,9 @@ __device__ __forceinline__ Run varlen_keys(const Sched& s, int32_t i) {
 
 // Key/value run visited at position v of rank's ring order.  Outside explicit
 // mode the key/value tensor is in natural order, so row index == position.
+// Ring modes take 0 <= rank < W and 0 <= v < num_visits, so the source rank
+// (rank - step) mod W is rank - step, plus W when that is negative (no
+// integer division, which the GPU does in software).
 RATTN_HD Run visit(const Sched& s, int32_t rank, int32_t v) {
   Run r;
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -104,13 +107,15 @@ RATTN_HD Run visit(const Sched& s, int32_t rank, int32_t v) {
   if (s.mode == kVisitExplicit) {
     r = s.kruns[v];
   } else if (s.mode == kVisitContiguousRing) {
-    int32_t src = ((rank - v) % s.W + s.W) % s.W;
+    int32_t src = rank - v;
+    if (src < 0) src += s.W;
     r.row0 = (int64_t)src * s.blk;
     r.len = s.blk;
     r.pos0 = r.row0;
   } else {
     int32_t step = v >> 1;
-    int32_t src = ((rank - step) % s.W + s.W) % s.W;
+    int32_t src = rank - step;
+    if (src < 0) src += s.W;
     int32_t chunk = (v & 1) ? (2 * s.W - 1 - src) : src;
     r.row0 = (int64_t)chunk * s.blk;
     r.len = s.blk;
@@ -139,7 +144,9 @@ struct QTile {
   int32_t rank;
 };
 
-RATTN_HD QTile query_tile(const Sched& s, int32_t t) {
+// br: query rows per tile, the s.br the schedule was built with; kernels pass
+// it as a compile-time constant, so that the divisions by it are shifts.
+RATTN_HD QTile query_tile(const Sched& s, int32_t t, int32_t br) {
   QTile qt;
 #if defined(__HIP_DEVICE_COMPILE__)
   if (s.mode == kVisitVarlen) {
@@ -150,27 +157,31 @@ RATTN_HD QTile query_tile(const Sched& s, int32_t t) {
     int64_t lq = s.vl_q_len[i];
     if (st < 0 || st > s.vl_nq) lq = 0;
     if (lq > s.vl_nq - st) lq = s.vl_nq - st;
-    const int64_t nt = (lq + s.br - 1) / s.br;
+    const int64_t nt = (lq + br - 1) / br;
     if (s.reverse) lt = nt - 1 - lt;  // causal: latest (longest) tiles first
-    qt.row0 = st + lt * s.br;
-    const int64_t rem = lq - lt * s.br;
-    qt.rows = (lt < 0 || lt >= nt) ? 0 : (rem < s.br ? rem : s.br);
-    qt.pos0 = varlen_keys(s, i).len - lq + lt * s.br;
+    qt.row0 = st + lt * br;
+    const int64_t rem = lq - lt * br;
+    qt.rows = (lt < 0 || lt >= nt) ? 0 : (rem < br ? rem : br);
+    qt.pos0 = varlen_keys(s, i).len - lq + lt * br;
     qt.rank = i;
     return qt;
   }
 #endif
-  int32_t i = 0;
-  for (; i + 1 < s.n_qseg; ++i)
-    if (t < s.qseg[i + 1].tile_begin) break;
+  // segment i: the last one whose tile_begin <= t (binary search; tile_begin
+  // increases with i and qseg[0].tile_begin = 0)
+  int32_t i = 0, hi = s.n_qseg;
+  while (hi - i > 1) {
+    const int32_t mid = (i + hi) >> 1;
+    if (t < s.qseg[mid].tile_begin) hi = mid; else i = mid;
+  }
   const QSeg& g = s.qseg[i];
-  int64_t nt = (g.len + s.br - 1) / s.br;
+  int64_t nt = (g.len + br - 1) / br;
   int64_t lt = t - g.tile_begin;
   if (s.reverse) lt = nt - 1 - lt;
-  qt.row0 = g.row0 + lt * s.br;
-  int64_t rem = g.len - lt * s.br;
-  qt.rows = rem < s.br ? rem : s.br;
-  qt.pos0 = g.pos0 + lt * s.br;
+  qt.row0 = g.row0 + lt * br;
+  int64_t rem = g.len - lt * br;
+  qt.rows = rem < br ? rem : br;
+  qt.pos0 = g.pos0 + lt * br;
   qt.rank = g.rank;
   return qt;
 }
