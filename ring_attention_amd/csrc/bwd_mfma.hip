@@ -211,22 +211,36 @@ __device__ __forceinline__ void work_order(int32_t BH, int64_t n_tiles, bool hea
 }
 
 // ---- dK, dV ------------------------------------------------------------------
+// Eight wavefronts, 128 keys per workgroup.  K and V of the workgroup's keys
+// sit in LDS (64 KB) and are read as the B operand of S = Q K^T and
+// dP = dO V^T, so that a wave holds only its dK and dV accumulators and two
+// waves fit per SIMD.  Wave w takes keys 32 (w % 4) .. +31 and query rows
+// 32 (w / 4) .. +31 of every 64-row query tile; waves w and w + 4 add their
+// dK and dV through LDS at the end.
+constexpr int kThreadsKV = 512;
+
 template <typename TT, bool ACC, bool BUF>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
+__global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkv_mfma_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, const typename TT::elem* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, void* __restrict__ dk,
     void* __restrict__ dv, BwdParams p) {
   using E = typename TT::elem;
   using v8 = typename TT::v8;
-  constexpr int kStat = 2 * kTileBytes;          // lse, then D, 64 floats each
+  constexpr int kKV = 2 * kOwn * kRowBytes;      // K, then V, of the owned keys: 64 KB
+  constexpr int kStat = 2 * kTileBytes;          // in a query buffer: lse, then D, 64 floats each
   constexpr int kBufBytes = kStat + 2 * kRows * 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
+  constexpr int kSmem = kKV + 2 * kBufBytes;
+  constexpr int kRed = 4 * 2 * DB * 16 * 64 * 4;  // dK, dV of waves 4..7
+  static_assert(kRed <= kSmem, "the dK, dV hand-over fits in the tiles' LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;   // key group: keys 32 kg .. +31
+  const int qh = wave >> 2;  // query half of every query tile
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
@@ -242,26 +256,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
   // live in scratch, and the compiler's wait for a scratch load would also
   // wait for the tile DMA issued before it
   const BwdRun qr0 = item.other[0], qr1 = item.other[1];
-  const int wk0 = 32 * wave;
+  const int wk0 = 32 * kg;
   const int wkrows = kt.rows - wk0 < 0 ? 0 : (kt.rows - wk0 > 32 ? 32 : (int)(kt.rows - wk0));
   const bool k_valid = l32 < wkrows;
   const int64_t wkpos = kt.pos0 + wk0;      // position of the wave's first key
   const int64_t kpos = wkpos + l32;         // this lane's key
-  const int64_t krow =
-      ((int64_t)b * p.k_rows + p.k_off + kt.row0 + wk0 + (k_valid ? l32 : 0)) * p.Hkv + hkv;
+  const int64_t krow0 = (int64_t)b * p.k_rows + p.k_off + kt.row0;  // first owned key row
+  const int64_t krow = (krow0 + wk0 + (k_valid ? l32 : 0)) * p.Hkv + hkv;
 
-  // this lane's key as the B operand: 8 dims 16 ks + 8 hl .. +7
-  v8 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (k_valid) {
-      kf[ks] = *(const v8*)(k + krow * D + 16 * ks + 8 * hl);
-      vf[ks] = *(const v8*)(v + krow * D + 16 * ks + 8 * hl);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = (typename TT::elem)0.f;
-    }
-  }
   f32x16 dka[DB], dva[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16{};
@@ -305,89 +307,120 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
   };
   const int64_t qstride = (int64_t)p.Hq * D;
   const v4i qrs = BUF ? tensor_rsrc(q) : v4i{}, grs = BUF ? tensor_rsrc(dout) : v4i{};
+  // query tile t into buffer buf: waves 0-3 move Q, waves 4-7 dO (16 rows
+  // each), wave 0 the lse and wave 4 the D values of its rows
   auto issue = [&](int64_t t, int buf) {
     const QT x = tile_of(t);
-    const uint32_t base = smem_addr + buf * kBufBytes;
-    dma_tile<BUF>(q, qrs, (int64_t)x.hq * D, x.row0, x.rows, qstride, base, wave, lane);
-    dma_tile<BUF>(dout, grs, (int64_t)x.hq * D, x.row0, x.rows, qstride, base + kTileBytes, wave,
-                  lane);
-    if (wave < 2) {
+    const uint32_t base = smem_addr + kKV + buf * kBufBytes;
+    if (qh == 0)
+      dma_tile<BUF>(q, qrs, (int64_t)x.hq * D, x.row0, x.rows, qstride, base, kg, lane);
+    else
+      dma_tile<BUF>(dout, grs, (int64_t)x.hq * D, x.row0, x.rows, qstride, base + kTileBytes, kg,
+                    lane);
+    if (kg == 0) {
       const int rc = lane < x.rows ? lane : x.rows - 1;
-      const float* src = (wave == 0 ? lse : delta) + (x.row0 + rc) * p.Hq + x.hq;
-      dma4(src, base + kStat + wave * kRows * 4);
+      const float* src = (qh == 0 ? lse : delta) + (x.row0 + rc) * p.Hq + x.hq;
+      dma4(src, base + kStat + qh * kRows * 4);
     }
   };
 
   const FragOff fo = frag_offsets(lane);
+  const char* kb_l = smem;                      // K rows of the owned keys
+  const char* vb_l = smem + kOwn * kRowBytes;   // V rows
   auto compute = [&](int64_t t, int buf) {
     const QT x = tile_of(t);
-    const char* qb_l = smem + buf * kBufBytes;
+    const char* qb_l = smem + kKV + buf * kBufBytes;
     const char* gb_l = qb_l + kTileBytes;
     const float* lse_l = (const float*)(qb_l + kStat);
     const float* dl_l = lse_l + kRows;
-    if (wkrows == 0) return;
-    if (p.causal && x.pos0 + x.rows - 1 < wkpos) return;  // no query of the tile sees a key
+    const int qb = qh;
+    if (wkrows == 0 || 32 * qb >= x.rows) return;
+    if (p.causal && x.pos0 + 32 * qb + 31 < wkpos) return;  // no row of the block sees a key
     const bool need_mask = x.rows < kRows || (p.causal && x.pos0 < wkpos + wkrows - 1);
+    // S and dP over the 8 k-steps: the four operands of a step (Q, K, dO, V
+    // fragments) are read two steps ahead, and the issue order is pinned, so
+    // that the reads stay a bounded number of registers
+    f32x16 s_acc = {}, dp_acc = {};
+    v8 fq[2], fk[2], fg[2], fv[2];
+    auto ld_s = [&](int ks, int slot) {
+      fq[slot] = row_frag<TT>(qb_l, fo, ks, qb);
+      fk[slot] = row_frag<TT>(kb_l, fo, ks, kg);
+      fg[slot] = row_frag<TT>(gb_l, fo, ks, qb);
+      fv[slot] = row_frag<TT>(vb_l, fo, ks, kg);
+    };
+    ld_s(0, 0);
+    ld_s(1, 1);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      if (32 * qb >= x.rows) break;
-      if (p.causal && x.pos0 + 32 * qb + 31 < wkpos) continue;
-      f32x16 s_acc = {}, dp_acc = {};
+    for (int ks = 0; ks < KS; ++ks) {
+      const int slot = ks & 1;
+      s_acc = TT::mfma32x32x16(fq[slot], fk[slot], s_acc);
+      dp_acc = TT::mfma32x32x16(fg[slot], fv[slot], dp_acc);
+      if (ks + 2 < KS) ld_s(ks + 2, slot);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // query row of register r: 32 qb + 8 (r/4) + 4 hl + r%4
+    f32x4 lv[4], dv4[4];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s_acc = TT::mfma32x32x16(row_frag<TT>(qb_l, fo, ks, qb), kf[ks], s_acc);
-        dp_acc = TT::mfma32x32x16(row_frag<TT>(gb_l, fo, ks, qb), vf[ks], dp_acc);
+    for (int j = 0; j < 4; ++j) {
+      lv[j] = *(const f32x4*)(lse_l + 32 * qb + 8 * j + 4 * hl);
+      dv4[j] = *(const f32x4*)(dl_l + 32 * qb + 8 * j + 4 * hl);
+    }
+    // P and dS of the block, each step over all 16 registers at once so
+    // that the independent chains overlap.  Register r of a lane holds
+    // query row 32 qb + 8 (r/4) + 4 hl + r%4, visible iff the row exists
+    // and (causal) the key is not after it: r2 = 8 (r/4) + r%4 in
+    // [rel, rlim) with rel = kpos - (x.pos0 + 32 qb + 4 hl).
+    float pr[16], ds[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      pr[rr] = fmaf(s_acc[rr], p.c, -lse2_of(lv[rr >> 2][rr & 3]));
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) pr[rr] = exp2_fast(pr[rr]);
+    if (need_mask) {
+      const int64_t rel64 = kpos - (x.pos0 + 32 * qb + 4 * hl);
+      const int rel = p.causal ? (rel64 > 64 ? 64 : (rel64 < -64 ? -64 : (int)rel64)) : -64;
+      const int rlim = x.rows - 32 * qb - 4 * hl;  // rows r2 < rlim exist
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int r2 = 8 * (rr >> 2) + (rr & 3);
+        pr[rr] = ((r2 >= rel) & (r2 < rlim)) ? pr[rr] : 0.f;
       }
-      // query row of register r: 32 qb + 8 (r/4) + 4 hl + r%4
-      f32x4 lv[4], dv4[4];
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lv[j] = *(const f32x4*)(lse_l + 32 * qb + 8 * j + 4 * hl);
-        dv4[j] = *(const f32x4*)(dl_l + 32 * qb + 8 * j + 4 * hl);
-      }
-      // P and dS of the block, each step over all 16 registers at once so
-      // that the independent chains overlap.  Register r of a lane holds
-      // query row 32 qb + 8 (r/4) + 4 hl + r%4, visible iff the row exists
-      // and (causal) the key is not after it: r2 = 8 (r/4) + r%4 in
-      // [rel, rlim) with rel = kpos - (x.pos0 + 32 qb + 4 hl).
-      float pr[16], ds[16];
+    for (int rr = 0; rr < 16; ++rr) ds[rr] = pr[rr] * (dp_acc[rr] - dv4[rr >> 2][rr & 3]);
+    float pw[8], dw[8];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        pr[rr] = fmaf(s_acc[rr], p.c, -lse2_of(lv[rr >> 2][rr & 3]));
+    for (int r = 0; r < 16; r += 2) {
+      pack_pair<TT>(&pw[r >> 1], pr[r], pr[r + 1]);
+      pack_pair<TT>(&dw[r >> 1], ds[r], ds[r + 1]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over (u, db): the two transposed
+    // operands of a step read two steps ahead, issue order pinned
+    v8 tg[2], tq[2];
+    auto ld_t = [&](int i, int slot) {
+      tg[slot] = tr_frag<TT>(gb_l, fo, i % DB, 2 * qb + i / DB);
+      tq[slot] = tr_frag<TT>(qb_l, fo, i % DB, 2 * qb + i / DB);
+    };
+    ld_t(0, 0);
+    ld_t(1, 1);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) pr[rr] = exp2_fast(pr[rr]);
-      if (need_mask) {
-        const int64_t rel64 = kpos - (x.pos0 + 32 * qb + 4 * hl);
-        const int rel = p.causal ? (rel64 > 64 ? 64 : (rel64 < -64 ? -64 : (int)rel64)) : -64;
-        const int rlim = x.rows - 32 * qb - 4 * hl;  // rows r2 < rlim exist
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int r2 = 8 * (rr >> 2) + (rr & 3);
-          pr[rr] = ((r2 >= rel) & (r2 < rlim)) ? pr[rr] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) ds[rr] = pr[rr] * (dp_acc[rr] - dv4[rr >> 2][rr & 3]);
-      float pw[8], dw[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        pack_pair<TT>(&pw[r >> 1], pr[r], pr[r + 1]);
-        pack_pair<TT>(&dw[r >> 1], ds[r], ds[r + 1]);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const v8 pu = packed_operand<TT>(pw, u);
-        const v8 du = packed_operand<TT>(dw, u);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dva[db] = TT::mfma32x32x16(tr_frag<TT>(gb_l, fo, db, 2 * qb + u), pu, dva[db]);
-          dka[db] = TT::mfma32x32x16(tr_frag<TT>(qb_l, fo, db, 2 * qb + u), du, dka[db]);
-        }
-      }
+    for (int i = 0; i < 2 * DB; ++i) {
+      const int slot = i & 1, u = i / DB, db = i % DB;
+      dva[db] = TT::mfma32x32x16(tg[slot], packed_operand<TT>(pw, u), dva[db]);
+      dka[db] = TT::mfma32x32x16(tq[slot], packed_operand<TT>(dw, u), dka[db]);
+      if (i + 2 < 2 * DB) ld_t(i + 2, slot);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   if (T > 0) {
+    // the owned keys' K and V rows (rows past the last key repeat it: finite
+    // values whose results are not stored), then query tile 0
+    const int64_t kstride = (int64_t)p.Hkv * D;
+    const v4i krs = BUF ? tensor_rsrc(k) : v4i{}, vrs = BUF ? tensor_rsrc(v) : v4i{};
+    dma_tile<BUF>(k, krs, (int64_t)hkv * D, krow0, kt.rows, kstride, smem_addr, wave, lane);
+    dma_tile<BUF>(v, vrs, (int64_t)hkv * D, krow0, kt.rows, kstride,
+                  smem_addr + kOwn * kRowBytes, wave, lane);
     issue(0, 0);
     wait_dma();
     __syncthreads();
@@ -399,7 +432,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma_kernel(
     }
   }
 
-  if (!k_valid) return;
+  // waves 4..7 hand their sums to waves 0..3 (every tile read is done: the
+  // loop ends with a barrier; with no tile no DMA was issued)
+  float* red = (float*)smem + (size_t)kg * (2 * DB * 16 * 64);
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[(db * 16 + r) * 64 + lane] = dka[db][r];
+        red[((DB + db) * 16 + r) * 64 + lane] = dva[db][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 1 || !k_valid) return;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dka[db][r] += red[(db * 16 + r) * 64 + lane];
+      dva[db][r] += red[((DB + db) * 16 + r) * 64 + lane];
+    }
   // lane: key l%32; register 4 j + e of block db: dim 32 db + 8 j + 4 hl + e
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -627,11 +680,11 @@ hipError_t launch_acc(const void* q, const void* k, const void* v, const void* d
   if (kb > 0) {
     if (buf)
       hipLaunchKernelGGL((bwd_dkv_mfma_kernel<TT, ACC, true>), dim3((unsigned)kb),
-                         dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                         dim3(kThreadsKV), 0, stream, (const E*)q, (const E*)k, (const E*)v,
                          (const E*)dout, lse, delta, dk, dv, p);
     else
       hipLaunchKernelGGL((bwd_dkv_mfma_kernel<TT, ACC, false>), dim3((unsigned)kb),
-                         dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                         dim3(kThreadsKV), 0, stream, (const E*)q, (const E*)k, (const E*)v,
                          (const E*)dout, lse, delta, dk, dv, p);
     return hipGetLastError();
   }
