@@ -49,21 +49,43 @@ namespace rattn {
 
 namespace {
 
-constexpr int D = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;    // 256 query rows per workgroup
 constexpr int BC = 64;              // keys per tile
-constexpr int kRowBytes = D * 2;
-constexpr int kTileBytes = BC * kRowBytes;  // 16 KB
-constexpr int kBufBytes = 2 * kTileBytes;   // K + V
 constexpr int kNBuf = 4;
-constexpr int KS = D / 16;
-constexpr int DB = D / 32;
 constexpr int NKB = BC / 32;
 constexpr int NU = BC / 16;
-constexpr int kDmaBlocks = kBufBytes / 1024;          // 32 per tile
-constexpr int kDmaPerWave = kDmaBlocks / kWaves;      // 4 per wave per tile
+
+// Geometry of one head dimension D (128 or 64).  A K or V row is 2 D bytes,
+// D / 8 chunks of 16 bytes; one direct-to-LDS request moves 1 KB, 1024 / 2D
+// rows.  Chunk c of row r sits in LDS at chunk slot
+//   K: c ^ (r mod 16) for D = 128,    c ^ ((r / 2) mod 8) for D = 64,
+//   V: c ^ 4 (r mod 4) for D = 128,   c ^ 4 ((r / 2) mod 2) for D = 64,
+// so that a K fragment read (16 lanes per cycle: 16 rows, one chunk each)
+// and a transposing V read (32 lanes: 4 rows x 8 half-chunks) each touch
+// every LDS bank once.
+template <int D_>
+struct Geo {
+  static constexpr int D = D_;
+  static_assert(D == 128 || D == 64, "head dimensions of this kernel");
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kTileBytes = BC * kRowBytes;       // 16 KB, 8 KB
+  static constexpr int kBufBytes = 2 * kTileBytes;        // K + V
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;    // 4, 8
+  static constexpr int kDmaBlocks = kBufBytes / 1024;     // per tile: 32, 16
+  static constexpr int kDmaPerWave = kDmaBlocks / kWaves; // 4, 2
+  static constexpr int kBlocksPerTensor = kDmaPerWave / 2;
+  __device__ static int kslot(int c, int r) {
+    return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+  }
+  __device__ static int vslot(int c, int r) {
+    return D == 128 ? c ^ (4 * (r & 3)) : c ^ (4 * ((r >> 1) & 1));
+  }
+};
 
 static_assert(kBr == kMfma128Br, "schedule built for this tile height");
 
@@ -105,8 +127,14 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t soff, uint32_t voff, ui
                : "memory");
 }
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// N = this wave's DMA requests of one tile, which may stay in flight
+template <int N>
 __device__ __forceinline__ void wait_dma_but_one_tile() {
-  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // kDmaPerWave DMAs may stay in flight
+  static_assert(N == 4 || N == 2, "requests per wave per tile");
+  if constexpr (N == 4)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
 }
 __device__ __forceinline__ void slot_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -200,8 +228,10 @@ __device__ __forceinline__ void run_next(RunCursor& c, const RunCursorCtx& x) {
   if (c.t >= c.nt) run_settle(c, x);
 }
 
-template <typename TT, bool OUT_F32, bool BUF>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
+// D = 64: 64 KB of LDS and at most 128 registers per wave, two workgroups per
+// compute unit (four waves per SIMD); D = 128: one workgroup, two waves per SIMD.
+template <typename TT, int D, bool OUT_F32, bool BUF>
+__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
     FwdParams p, Sched s) {
@@ -209,6 +239,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   using v8 = typename TT::v8;
   using v4 = typename TT::v4;
   using E2 = typename TT::v2;
+  using G = Geo<D>;
+  constexpr int kRowBytes = G::kRowBytes;
+  constexpr int kTileBytes = G::kTileBytes;
+  constexpr int kBufBytes = G::kBufBytes;
+  constexpr int KS = G::KS;
+  constexpr int DB = G::DB;
+  constexpr int kDmaPerWave = G::kDmaPerWave;
+  constexpr int NBW = G::kBlocksPerTensor;  // this wave's K (and V) blocks of a tile
 
   __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kBufBytes];
   const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
@@ -261,14 +299,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   const char* kbase = (const char*)(k + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D);
   const char* vbase = (const char*)(v + (int64_t)b * p.Nk * kv_stride + (int64_t)hkv * D);
   const uint32_t row_bytes = (uint32_t)(kv_stride * sizeof(E));
-  uint32_t kdma_off[2], vdma_off[2];
-  int dma_row[2];
+  // Block b of a tile's K (V) half is rows kRowsPerDma b .. +kRowsPerDma-1;
+  // lane l lands in LDS slot l mod kChunks of row kRowsPerDma b + l / kChunks
+  // and therefore reads the source chunk stored at that slot (the swizzles
+  // are their own inverses).
+  uint32_t kdma_off[NBW], vdma_off[NBW];
+  int dma_row[NBW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 4 * (2 * wave + i) + (lane >> 4);
+  for (int i = 0; i < NBW; ++i) {
+    const int slot = lane % G::kChunks;
+    const int r = G::kRowsPerDma * (NBW * wave + i) + lane / G::kChunks;
     dma_row[i] = r;
-    kdma_off[i] = (uint32_t)r * row_bytes + 16 * (l16 ^ (r & 15));
-    vdma_off[i] = (uint32_t)r * row_bytes + 16 * (l16 ^ (4 * (r & 3)));
+    kdma_off[i] = (uint32_t)r * row_bytes + 16 * G::kslot(slot, r);
+    vdma_off[i] = (uint32_t)r * row_bytes + 16 * G::vslot(slot, r);
   }
   // This wave's four 16-byte-per-lane DMA parts of one tile: part 2i is K
   // block 2w+i, part 2i+1 is V block 2w+i.
@@ -300,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   uint32_t k_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    k_off[ks] = (uint32_t)(l32 * kRowBytes + 16 * ((2 * ks + hl) ^ (l32 & 15)));
+    k_off[ks] = (uint32_t)(l32 * kRowBytes + 16 * G::kslot(2 * ks + hl, l32));
   uint32_t v_off[DB];
   {
     const int qrow = l16 >> 2;
@@ -310,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db)
       v_off[db] = (uint32_t)(kTileBytes + (4 * hl + qrow) * kRowBytes +
-                             16 * ((4 * db + c_in) ^ (4 * qrow)) + half);
+                             16 * G::vslot(4 * db + c_in, 4 * hl + qrow) + half);
   }
 
   // ---- tile bookkeeping ----------------------------------------------------
@@ -348,18 +391,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
       // precomputed (no per-tile vector work)
       const uint32_t t_off = (uint32_t)(dp.krow0 * (int64_t)row_bytes);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        dma16(krs, t_off, kdma_off[i], dp.lds + (2 * wave + i) * 1024);
-        dma16(vrs, t_off, vdma_off[i], dp.lds + kTileBytes + (2 * wave + i) * 1024);
+      for (int i = 0; i < NBW; ++i) {
+        dma16(krs, t_off, kdma_off[i], dp.lds + (NBW * wave + i) * 1024);
+        dma16(vrs, t_off, vdma_off[i], dp.lds + kTileBytes + (NBW * wave + i) * 1024);
       }
       return;
     }
     const int last = dp.rem - 1;
     const int64_t tb = dp.krow0 * (int64_t)row_bytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NBW; ++i) {
       const uint32_t back = dma_row[i] > last ? (uint32_t)(dma_row[i] - last) * row_bytes : 0u;
-      const uint32_t lk = dp.lds + (2 * wave + i) * 1024;
+      const uint32_t lk = dp.lds + (NBW * wave + i) * 1024;
       if (BUF) {
         dma16(krs, (uint32_t)tb, kdma_off[i] - back, lk);
         dma16(vrs, (uint32_t)tb, vdma_off[i] - back, lk + kTileBytes);
@@ -379,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   }
   issue_all(plan_next());  // tile 0
   issue_all(plan_next());  // tile 1
-  if (T > 1) wait_dma_but_one_tile(); else wait_dma_all();
+  if (T > 1) wait_dma_but_one_tile<kDmaPerWave>(); else wait_dma_all();
   __syncthreads();
 
   // per-group state carried between phases
@@ -535,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   // Before the window in which the groups score tile j, tile j must have
   // landed on every wave; only tile j+1's requests may still be in flight.
   auto wait_tile = [&](int j) {
-    if (j + 1 < T) wait_dma_but_one_tile(); else wait_dma_all();
+    if (j + 1 < T) wait_dma_but_one_tile<kDmaPerWave>(); else wait_dma_all();
   };
 
   // Windows.  Window 0 is group A's M0, window 1 A's V0 and B's M0; window
@@ -600,7 +643,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma128_kernel(
   if (hl == 0) lse_w[orow] = mw.lse;
 }
 
-template <typename TT>
+template <typename TT, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse,
                     bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
   using E = typename TT::elem;
@@ -612,26 +655,29 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
   const dim3 g((unsigned)blocks), t(kThreads);
   const E *qe = (const E*)q, *ke = (const E*)k, *ve = (const E*)v;
   if (out_f32 && buf)
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, true, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, D, true, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   else if (out_f32)
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, true, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, D, true, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   else if (buf)
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, false, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, D, false, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   else
-    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, false, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_mfma128_kernel<TT, D, false, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_mfma128(int dtype, const void* q, const void* k, const void* v, void* out,
-                              float* lse, bool out_f32, const FwdParams& p, const Sched& s,
-                              hipStream_t stream) {
-  switch (dtype) {
-    case 1: return launch_t<F16>(q, k, v, out, lse, out_f32, p, s, stream);
-    case 2: return launch_t<Bf16>(q, k, v, out, lse, out_f32, p, s, stream);
-    default: return hipErrorInvalidValue;
+hipError_t launch_fwd_mfma128(int dtype, int d, const void* q, const void* k, const void* v,
+                              void* out, float* lse, bool out_f32, const FwdParams& p,
+                              const Sched& s, hipStream_t stream) {
+  if (d == 128) {
+    if (dtype == 1) return launch_t<F16, 128>(q, k, v, out, lse, out_f32, p, s, stream);
+    if (dtype == 2) return launch_t<Bf16, 128>(q, k, v, out, lse, out_f32, p, s, stream);
+  } else if (d == 64) {
+    if (dtype == 1) return launch_t<F16, 64>(q, k, v, out, lse, out_f32, p, s, stream);
+    if (dtype == 2) return launch_t<Bf16, 64>(q, k, v, out, lse, out_f32, p, s, stream);
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace rattn

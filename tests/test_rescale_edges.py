@@ -1,5 +1,5 @@
-"""d = 128 forward kernel vs the fp64 oracle where the online softmax's
-running maximum moves (needs a GPU).
+"""The direct-to-LDS forward kernel (d = 128 and d = 64) vs the fp64 oracle
+where the online softmax's running maximum moves (needs a GPU).
 
 The kernel keeps a running row max m and rescales the accumulator by
 exp(m_old - m_new) only when a score exceeds m by more than a slack (lazy
@@ -72,25 +72,29 @@ def run_all_paths(q, k, v, scale, what, W=2):
             check(out, lse, ref_o, ref_l, f"{what} ring steps rank={r} fused={fused}")
 
 
+HEAD_DIMS = [128, 64]
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_d128_large_magnitude_scores(gpu, dtype):
+def test_large_magnitude_scores(gpu, dtype, d):
     """q, k ~ N(0, 10^2): scores of several hundred, softmax close to argmax."""
     g = torch.Generator().manual_seed(61)
     N = 2 * 256 + 88  # three query tiles, ragged last tile; 9 key tiles + 24
-    q = (torch.randn(1, N, 4, 128, generator=g) * 10).to(dtype)
-    k = (torch.randn(1, N, 2, 128, generator=g) * 10).to(dtype)
-    v = torch.randn(1, N, 2, 128, generator=g).to(dtype)
-    run_all_paths(q, k, v, None, f"large scores {dtype}")
+    q = (torch.randn(1, N, 4, d, generator=g) * 10).to(dtype)
+    k = (torch.randn(1, N, 2, d, generator=g) * 10).to(dtype)
+    v = torch.randn(1, N, 2, d, generator=g).to(dtype)
+    run_all_paths(q, k, v, None, f"large scores d={d} {dtype}")
 
 
+@pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_d128_max_moves_every_key_tile(gpu, dtype):
+def test_max_moves_every_key_tile(gpu, dtype, d):
     """A score ramp: every 64-key tile's scores exceed all earlier ones by
     more than 8 base-2 units (6.4 natural units per tile), so the running
     max moves, and the accumulator is rescaled, on every key tile."""
     g = torch.Generator().manual_seed(62)
     N = 640
-    d = 128
     q = torch.zeros(1, N, 2, d)
     q[..., 0] = 1.0
     q[..., 1:] = torch.randn(1, N, 2, d - 1, generator=g) * 0.05
@@ -98,7 +102,7 @@ def test_d128_max_moves_every_key_tile(gpu, dtype):
     # score of key j for every query: scale * k_j[0] = 0.1 j (+ small noise)
     k[0, :, 0, 0] = 0.1 * torch.arange(N, dtype=torch.float32) * math.sqrt(d)
     v = torch.randn(1, N, 1, d, generator=g)
-    run_all_paths(q.to(dtype), k.to(dtype), v.to(dtype), None, f"ramp {dtype}")
+    run_all_paths(q.to(dtype), k.to(dtype), v.to(dtype), None, f"ramp d={d} {dtype}")
 
 
 # Raise of each key tile's scores over the first tile's, in base-2 units of
@@ -108,14 +112,15 @@ def test_d128_max_moves_every_key_tile(gpu, dtype):
 JUMPS = [0.0, 1.0, 1.9375, 2.0, 2.0625, 3.0, 7.9375, 8.0, 8.0625, 12.0, 12.0, 20.125, 19.0]
 
 
+@pytest.mark.parametrize("d", HEAD_DIMS)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_d128_thresholds_of_lazy_rescaling(gpu, dtype):
+def test_thresholds_of_lazy_rescaling(gpu, dtype, d):
     """Every key tile holds 64 equal scores J_t (base-2 units; q = e_0, the
     scale ln2 / 16 and k_j[0] = 16 J_t, all exact in 16 bits), with J_t
     stepping through the values above, below and at the thresholds.  Every
     query is e_0, so all rows see the same scores (causal rows a prefix)."""
     g = torch.Generator().manual_seed(63)
-    d, T = 128, len(JUMPS)
+    T = len(JUMPS)
     N = 64 * T
     q = torch.zeros(1, N, 2, d)
     q[..., 0] = 1.0
@@ -124,16 +129,16 @@ def test_d128_thresholds_of_lazy_rescaling(gpu, dtype):
         k[0, 64 * t:64 * (t + 1), 0, 0] = 16.0 * j
     k[..., 1:] = torch.randn(1, N, 1, d - 1, generator=g)  # not seen by q = e_0
     v = torch.randn(1, N, 1, d, generator=g)
-    run_all_paths(q.to(dtype), k.to(dtype), v.to(dtype), LN2 / 16, f"thresholds {dtype}")
+    run_all_paths(q.to(dtype), k.to(dtype), v.to(dtype), LN2 / 16, f"thresholds d={d} {dtype}")
 
 
-def test_d128_tile_sums_at_the_slow_path_bound(gpu):
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_tile_sums_at_the_slow_path_bound(gpu, d):
     """Scores spread so that some lanes' tile sums land just below and just
     above the exact-max bound while no single p comes near 2^8: per key
     tile, key i has score log2 of a value that makes the 32 keys of a lane
     sum to 127, 128 or 129 times the first tile's p."""
     g = torch.Generator().manual_seed(64)
-    d = 128
     base = np.zeros(64)
     tiles = [base]
     for target in (127.0, 128.0, 129.0, 64.0, 200.0):
@@ -149,4 +154,4 @@ def test_d128_tile_sums_at_the_slow_path_bound(gpu):
     k[..., 1:] = torch.randn(1, N, 1, d - 1, generator=g)
     v = torch.randn(1, N, 1, d, generator=g)
     for dtype in (torch.bfloat16, torch.float16):
-        run_all_paths(q.to(dtype), k.to(dtype), v.to(dtype), LN2 / 16, f"tile sums {dtype}")
+        run_all_paths(q.to(dtype), k.to(dtype), v.to(dtype), LN2 / 16, f"tile sums d={d} {dtype}")
