@@ -57,18 +57,18 @@ constexpr int kNBuf = 4;
 constexpr int NKB = BC / 32;
 constexpr int NU = BC / 16;
 
-// Geometry of one head dimension D (128 or 64).  A K or V row is 2 D bytes,
-// D / 8 chunks of 16 bytes; one direct-to-LDS request moves 1 KB, 1024 / 2D
-// rows.  Chunk c of row r sits in LDS at chunk slot
-//   K: c ^ (r mod 16) for D = 128,    c ^ ((r / 2) mod 8) for D = 64,
-//   V: c ^ 4 (r mod 4) for D = 128,   c ^ 4 ((r / 2) mod 2) for D = 64,
+// Geometry of one head dimension D (128, 64 or 32).  A K or V row is 2 D
+// bytes, D / 8 chunks of 16 bytes; one direct-to-LDS request moves 1 KB,
+// 1024 / 2D rows.  Chunk c of row r sits in LDS at chunk slot
+//   K: c ^ (r mod 16) (D = 128),  c ^ ((r / 2) mod 8) (D = 64),  c ^ ((r / 4) mod 4) (D = 32),
+//   V: c ^ 4 (r mod 4) (D = 128), c ^ 4 ((r / 2) mod 2) (D = 64), c (D = 32),
 // so that a K fragment read (16 lanes per cycle: 16 rows, one chunk each)
 // and a transposing V read (32 lanes: 4 rows x 8 half-chunks) each touch
 // every LDS bank once.
 template <int D_>
 struct Geo {
   static constexpr int D = D_;
-  static_assert(D == 128 || D == 64, "head dimensions of this kernel");
+  static_assert(D == 128 || D == 64 || D == 32, "head dimensions of this kernel");
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kChunks = D / 8;
   static constexpr int kTileBytes = BC * kRowBytes;       // 16 KB, 8 KB
@@ -76,14 +76,14 @@ struct Geo {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int kRowsPerDma = 1024 / kRowBytes;    // 4, 8
-  static constexpr int kDmaBlocks = kBufBytes / 1024;     // per tile: 32, 16
-  static constexpr int kDmaPerWave = kDmaBlocks / kWaves; // 4, 2
+  static constexpr int kDmaBlocks = kBufBytes / 1024;     // per tile: 32, 16, 8
+  static constexpr int kDmaPerWave = kDmaBlocks / kWaves; // 4, 2, 1
   static constexpr int kBlocksPerTensor = kDmaPerWave / 2;
   __device__ static int kslot(int c, int r) {
-    return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+    return D == 128 ? c ^ (r & 15) : (D == 64 ? c ^ ((r >> 1) & 7) : c ^ ((r >> 2) & 3));
   }
   __device__ static int vslot(int c, int r) {
-    return D == 128 ? c ^ (4 * (r & 3)) : c ^ (4 * ((r >> 1) & 1));
+    return D == 128 ? c ^ (4 * (r & 3)) : (D == 64 ? c ^ (4 * ((r >> 1) & 1)) : c);
   }
 };
 
@@ -130,11 +130,13 @@ __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0
 // N = this wave's DMA requests of one tile, which may stay in flight
 template <int N>
 __device__ __forceinline__ void wait_dma_but_one_tile() {
-  static_assert(N == 4 || N == 2, "requests per wave per tile");
+  static_assert(N == 4 || N == 2 || N == 1, "requests per wave per tile");
   if constexpr (N == 4)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else
+  else if constexpr (N == 2)
     asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
 }
 __device__ __forceinline__ void slot_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -246,7 +248,10 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
   constexpr int KS = G::KS;
   constexpr int DB = G::DB;
   constexpr int kDmaPerWave = G::kDmaPerWave;
-  constexpr int NBW = G::kBlocksPerTensor;  // this wave's K (and V) blocks of a tile
+  // this wave's K (and V) blocks of a tile; D = 32: one block, wave w moves
+  // block w mod 4 of K (w < 4) or of V
+  constexpr bool kOnePart = kDmaPerWave == 1;
+  constexpr int NBW = kOnePart ? 1 : G::kBlocksPerTensor;
 
   __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kBufBytes];
   const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
@@ -308,7 +313,8 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     const int slot = lane % G::kChunks;
-    const int r = G::kRowsPerDma * (NBW * wave + i) + lane / G::kChunks;
+    const int blk = kOnePart ? (wave & 3) : NBW * wave + i;
+    const int r = G::kRowsPerDma * blk + lane / G::kChunks;
     dma_row[i] = r;
     kdma_off[i] = (uint32_t)r * row_bytes + 16 * G::kslot(slot, r);
     vdma_off[i] = (uint32_t)r * row_bytes + 16 * G::vslot(slot, r);
@@ -386,6 +392,19 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
   };
   auto issue_all = [&](const DmaPlan& dp) {
     if (!dp.on) return;
+    if constexpr (kOnePart) {
+      const bool is_v = wave >= 4;
+      const uint32_t dst = dp.lds + (is_v ? kTileBytes : 0) + (wave & 3) * 1024;
+      const uint32_t off = is_v ? vdma_off[0] : kdma_off[0];
+      const int last = dp.full ? BC - 1 : dp.rem - 1;
+      const uint32_t back = dma_row[0] > last ? (uint32_t)(dma_row[0] - last) * row_bytes : 0u;
+      const int64_t tb = dp.krow0 * (int64_t)row_bytes;
+      if (BUF)
+        dma16(is_v ? vrs : krs, (uint32_t)tb, off - back, dst);
+      else
+        dma16((is_v ? vbase : kbase) + tb + (off - back), dst);
+      return;
+    }
     if (BUF && dp.full) {
       // full tile: its byte offset in the scalar soffset, lane offsets as
       // precomputed (no per-tile vector work)
@@ -676,6 +695,9 @@ hipError_t launch_fwd_mfma128(int dtype, int d, const void* q, const void* k, co
   } else if (d == 64) {
     if (dtype == 1) return launch_t<F16, 64>(q, k, v, out, lse, out_f32, p, s, stream);
     if (dtype == 2) return launch_t<Bf16, 64>(q, k, v, out, lse, out_f32, p, s, stream);
+  } else if (d == 32) {
+    if (dtype == 1) return launch_t<F16, 32>(q, k, v, out, lse, out_f32, p, s, stream);
+    if (dtype == 2) return launch_t<Bf16, 32>(q, k, v, out, lse, out_f32, p, s, stream);
   }
   return hipErrorInvalidValue;
 }

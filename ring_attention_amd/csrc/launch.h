@@ -8,19 +8,19 @@ namespace rattn {
 
 // Query rows per tile of each forward kernel; the schedule is built for it.
 constexpr int kGenericBr = 64;
-constexpr int kMfmaBr = 128;     // fwd_mfma (16-bit, d = 16, 32)
-constexpr int kMfma128Br = 256;  // fwd_mfma128 (16-bit, d = 64, 128)
+constexpr int kMfmaBr = 128;     // fwd_mfma (16-bit, d = 16)
+constexpr int kMfma128Br = 256;  // fwd_mfma128 (16-bit, d = 32, 64, 128)
 
 hipError_t launch_fwd_generic(int dtype, int d, const void* q, const void* k, const void* v,
                               void* out, float* lse, bool out_f32, const FwdParams& p,
                               const Sched& s, hipStream_t stream);
 
-// 16-bit inputs, d = 64 or 128 (direct-to-LDS tiles, transposing V reads).
+// 16-bit inputs, d = 32, 64 or 128 (direct-to-LDS tiles, transposing V reads).
 hipError_t launch_fwd_mfma128(int dtype, int d, const void* q, const void* k, const void* v,
                               void* out, float* lse, bool out_f32, const FwdParams& p,
                               const Sched& s, hipStream_t stream);
 
-// 16-bit inputs, d in {16, 32, 64, 128} (d = 64 and 128 are routed to
+// 16-bit inputs, d in {16, 32, 64, 128} (d = 32, 64 and 128 are routed to
 // launch_fwd_mfma128).
 hipError_t launch_fwd_mfma(int dtype, int d, const void* q, const void* k, const void* v,
                            void* out, float* lse, bool out_f32, const FwdParams& p,

@@ -71,7 +71,7 @@ bool use_mfma(int dtype, int d) { return dtype != RATTN_F32 && d >= 16; }
 // Query rows per tile of the kernel that will run (the schedule is built for it).
 int tile_rows(int dtype, int d) {
   if (!use_mfma(dtype, d)) return kGenericBr;
-  return d >= 64 ? kMfma128Br : kMfmaBr;
+  return d >= 32 ? kMfma128Br : kMfmaBr;
 }
 
 float resolve_scale(float scale, int d) {

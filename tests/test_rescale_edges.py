@@ -72,7 +72,7 @@ def run_all_paths(q, k, v, scale, what, W=2):
             check(out, lse, ref_o, ref_l, f"{what} ring steps rank={r} fused={fused}")
 
 
-HEAD_DIMS = [128, 64]
+HEAD_DIMS = [128, 64, 32]
 
 
 @pytest.mark.parametrize("d", HEAD_DIMS)
