@@ -19,8 +19,10 @@
 // A workgroup barrier ends every window (A's after its V phase, B's after
 // its M phase), one per key tile; inside a window the groups run unsynchronised.
 //
-// Every M phase runs the same 32-MFMA stream (a single code path keeps the
-// accumulators in place); a tile a wave does not score gets P = 0.  The
+// Every M phase inside the tile loop runs the same 32-MFMA stream (a single
+// code path keeps the accumulators in place); a tile a wave does not score
+// gets P = 0.  Group A's first phase skips the PV half and each group's
+// last phase the QK half, whose results would be unused.  The
 // stream reads each MFMA's LDS operand a few MFMAs ahead.  Scalar
 // bookkeeping sits in the V phase, next to the VALU work; each M phase
 // opens by issuing this wave's share of the DMA of a later tile.
@@ -431,10 +433,10 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
       }
     }
   };
-  // Every M phase runs the full MFMA stream (one code path keeps the
-  // accumulators in place).  The first PV therefore reads the V half of
-  // buffer kNBuf-1 with P = 0: zero it so that 0 * V stays 0 (no DMA targets
-  // that buffer before both groups' first M phase).
+  // Group B's first M phase runs the full MFMA stream (it sits in the tile
+  // loop), so its PV reads the V half of buffer kNBuf-1 with P = 0: zero it
+  // so that 0 * V stays 0 (no DMA targets that buffer before both groups'
+  // first M phase).
   {
     uint4* z = (uint4*)(smem + (kNBuf - 1) * kBufBytes + kTileBytes);
     for (int i = tid; i < kTileBytes / 16; i += kThreads) z[i] = uint4{0, 0, 0, 0};
@@ -498,21 +500,24 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
     }
   };
 
-  // M phase kk: PV of tile kk-1 (P = 0 for kk = 0 or a tile this wave did
-  // not score), then QK of tile kk (its scores are unused for kk = T).
+  // M phase kk: PV of tile kk-1 (P = 0 for a tile this wave did not score),
+  // then QK of tile kk.
   // The DMA of tile kk+2 (if any) is issued first.  The wave runs this
   // phase at raised priority, so that on its SIMD the issue arbiter prefers
   // its MFMAs over the partner wave's softmax VALU (oldest-first would favour
   // group A in both phases).
-  auto m_phase = [&](int kk) {
-    using yes = std::integral_constant<bool, true>;
+  // pv, qk: which halves run (both, except in group A's first phase, whose
+  // PV would multiply P = 0, and in each group's last, whose QK is unused).
+  auto m_phase = [&](int kk, auto pv, auto qk) {
     const char* pvb = smem + ((kk - 1) & (kNBuf - 1)) * kBufBytes;
     const char* qkb = smem + (kk & (kNBuf - 1)) * kBufBytes;
     __builtin_amdgcn_s_setprio(1);
     issue_all(plan_next());
-    mfma_stream(yes{}, yes{}, pvb, qkb);
+    mfma_stream(pv, qk, pvb, qkb);
     __builtin_amdgcn_s_setprio(0);
   };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
 
   // V phase: mask, running max (lazy rescale), exp, row sum, P of the tile
   // scored in the last M phase.
@@ -610,23 +615,29 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
   // is complete on every wave at the barrier ending window m, before any QK
   // of tile m (window m+1).  Both groups pass T+1 barriers.
   if (group == 0) {
-    m_phase(0);
+    m_phase(0, no{}, yes{});
     slot_barrier();
-    for (int j = 0; j < T; ++j) {
+    for (int j = 0; j + 1 < T; ++j) {
       v_phase();
       wait_tile(j + 1);
       slot_barrier();
-      m_phase(j + 1);  // requests tile j+3; for j+1 = T: PV of the last tile
+      m_phase(j + 1, yes{}, yes{});  // requests tile j+3
+    }
+    if (T > 0) {
+      v_phase();
+      wait_tile(T);
+      slot_barrier();
+      m_phase(T, yes{}, no{});  // PV of the last tile
     }
   } else {
     slot_barrier();
     for (int j = 0; j < T; ++j) {
-      m_phase(j);      // requests tile j+2
+      m_phase(j, yes{}, yes{});  // requests tile j+2
       wait_tile(j + 1);
       slot_barrier();
       v_phase();
     }
-    m_phase(T);        // PV of the last tile
+    m_phase(T, yes{}, no{});  // PV of the last tile
   }
   // ---- epilogue: O / l, LSE = m ln2 + ln l --------------------------------
   const float l_tot = pair_sum(l_run);
@@ -638,7 +649,19 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
   float* out_f = (float*)out + wi.split * p.split_out_stride;
   float* lse_w = lse + wi.split * p.split_lse_stride;
   const bool merging = OUT_F32 && p.merge_out;
-  const MergeW mw = merging ? merge_weights(lse_w[orow], lse_n) : MergeW{0.f, 1.f, lse_n};
+  // The running result this step merges into: every load is issued before
+  // the first use, so the row pays one memory latency, not one per chunk.
+  f32x4 prev[OUT_F32 ? DB * 4 : 1];
+  float lse_prev = kNegInf;
+  if (merging) {
+    lse_prev = lse_w[orow];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        prev[4 * db + j] = *(const f32x4*)(out_f + orow * D + 32 * db + 8 * j + 4 * hl);
+  }
+  const MergeW mw = merging ? merge_weights(lse_prev, lse_n) : MergeW{0.f, 1.f, lse_n};
   const float f_n = mw.f_n * inv;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -650,7 +673,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * f_n;
         f32x4* dst = (f32x4*)(out_f + orow * D + d0);
-        if (merging) o4 += *dst * mw.f_r;
+        if (merging) o4 += prev[4 * db + j] * mw.f_r;
         *dst = o4;
       } else {
         v4 o4;
