@@ -82,6 +82,30 @@ RATTN_API int rattn_fwd(const void* q, const void* k, const void* v, void* out, 
               void* stream);
 
 /*
+ * rattn_fwd with the work items (query tiles of every batch and head, as in
+ * the blockwise loop of the yz520gzy FlashAttention chapter) handed out from
+ * queues instead of one workgroup each: when the call (16-bit, d = 128) has
+ * more than twice as many query tiles as the GPU runs at once, a grid of that
+ * many workgroups
+ * takes them from eight counters (one per XCD; a workgroup whose XCD's queue
+ * is empty takes the others' remaining items), so that parts of the chip
+ * that run at a higher clock take more of the work instead of waiting at the
+ * end.  Smaller calls run exactly as rattn_fwd.  Results are identical to
+ * rattn_fwd's (every tile is computed by the same code).
+ *   queue_ws: DEVICE memory of at least RATTN_QUEUE_WS_BYTES bytes, 4-byte
+ *   aligned, owned by the caller; its contents on entry do not matter (the
+ *   call zeroes the counters on `stream` before the launch that uses them).
+ *   Calls that share a workspace must not overlap in time (consecutive calls
+ *   on one stream never do).  Other arguments, checks and status codes as
+ *   rattn_fwd; a missing or short workspace returns RATTN_EINVAL.
+ */
+#define RATTN_QUEUE_WS_BYTES 64
+RATTN_API int rattn_fwd_queued(const void* q, const void* k, const void* v, void* out,
+                               float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d,
+                               int dtype, float scale, int causal, int n_ring_steps, int zigzag,
+                               int rank, void* queue_ws, int64_t queue_ws_bytes, void* stream);
+
+/*
  * One ring step: the attention of a set of query rows over one received
  * key/value shard (the per-step block call of the Twinkle forward pass).
  *

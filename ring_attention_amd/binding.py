@@ -19,7 +19,7 @@ RATTN_OK, RATTN_EINVAL, RATTN_EUNSUPPORTED, RATTN_EHIP = 0, -1, -2, -3
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # Exported symbols, in the order include/rattn.h declares them.
-EXPORTS = ("rattn_fwd", "rattn_fwd_step", "rattn_fwd_step_merge", "rattn_merge",
+EXPORTS = ("rattn_fwd", "rattn_fwd_queued", "rattn_fwd_step", "rattn_fwd_step_merge", "rattn_merge",
            "rattn_fwd_varlen", "rattn_fwd_split", "rattn_fwd_split_noalloc",
            "rattn_split_hint", "rattn_bwd_delta",
            "rattn_bwd", "rattn_bwd_varlen", "rattn_bwd_step", "rattn_status_string")
@@ -54,6 +54,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rattn_fwd.restype = i32
     lib.rattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
                               i32, i32, i32, i32, vp]
+    lib.rattn_fwd_queued.restype = i32
+    lib.rattn_fwd_queued.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f32,
+                                     i32, i32, i32, i32, vp, i64, vp]
     lib.rattn_fwd_step.restype = i32
     lib.rattn_fwd_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i64, i64, i64,
                                    i64, i32, i32, f32, i32, i64p, i64p, i64p, i64p, vp]
@@ -147,6 +150,42 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                        int(bool(causal)), int(n_ring_steps), int(bool(zigzag)), int(rank),
                        _stream(q))
     _check("rattn_fwd", rc)
+    return out, lse
+
+
+QUEUE_WS_BYTES = 64  # RATTN_QUEUE_WS_BYTES
+
+
+def queue_workspace(device) -> torch.Tensor:
+    """A workspace for fwd_queued on `device` (its contents never matter)."""
+    return torch.empty(QUEUE_WS_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def fwd_queued(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+               n_ring_steps: int = 1, zigzag: bool = False, rank: int = -1,
+               scale: float | None = None, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None, queue_ws: torch.Tensor | None = None):
+    """fwd() with the query tiles handed out from per-XCD queues
+    (rattn_fwd_queued); queue_ws from queue_workspace() is allocated here
+    unless given.  Same result as fwd()."""
+    _qkv(q, k, v)
+    B, Nq, Hq, d = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    if queue_ws is None:
+        queue_ws = queue_workspace(q.device)
+    if queue_ws.device != q.device or not queue_ws.is_contiguous():
+        raise ValueError("queue_ws must be a contiguous tensor on q's device")
+    lib = load_library()
+    rc = lib.rattn_fwd_queued(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, Hq, Hkv, Nq, N, d, DTYPE_CODES[q.dtype],
+                              _scale(scale), int(bool(causal)), int(n_ring_steps),
+                              int(bool(zigzag)), int(rank), queue_ws.data_ptr(),
+                              queue_ws.numel() * queue_ws.element_size(), _stream(q))
+    _check("rattn_fwd_queued", rc)
     return out, lse
 
 

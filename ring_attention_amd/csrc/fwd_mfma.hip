@@ -348,9 +348,9 @@ hipError_t launch_d(int d, const void* q, const void* k, const void* v, void* ou
 
 hipError_t launch_fwd_mfma(int dtype, int d, const void* q, const void* k, const void* v,
                            void* out, float* lse, bool out_f32, const FwdParams& p,
-                           const Sched& s, hipStream_t stream) {
+                           const Sched& s, uint32_t* queues, hipStream_t stream) {
   if (d >= 32)
-    return launch_fwd_mfma128(dtype, d, q, k, v, out, lse, out_f32, p, s, stream);
+    return launch_fwd_mfma128(dtype, d, q, k, v, out, lse, out_f32, p, s, queues, stream);
   switch (dtype) {
     case 1: return launch_d<F16>(d, q, k, v, out, lse, out_f32, p, s, stream);
     case 2: return launch_d<Bf16>(d, q, k, v, out, lse, out_f32, p, s, stream);

@@ -232,13 +232,14 @@ __device__ __forceinline__ void run_next(RunCursor& c, const RunCursorCtx& x) {
   if (c.t >= c.nt) run_settle(c, x);
 }
 
-// D = 64: 64 KB of LDS and at most 128 registers per wave, two workgroups per
-// compute unit (four waves per SIMD); D = 128: one workgroup, two waves per SIMD.
+// One work item (a query tile of a (batch, head), or one key split of it):
+// work item `item` of the enumeration work_item_of describes.
 template <typename TT, int D, bool OUT_F32, bool BUF>
-__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel(
-    const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
-    const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
-    FwdParams p, Sched s) {
+__device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q,
+                                         const typename TT::elem* __restrict__ k,
+                                         const typename TT::elem* __restrict__ v,
+                                         void* __restrict__ out, float* __restrict__ lse,
+                                         const FwdParams& p, const Sched& s, uint32_t item) {
   using E = typename TT::elem;
   using v8 = typename TT::v8;
   using v4 = typename TT::v4;
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
 
   // ---- work item -------------------------------------------------------
   const int32_t BH = p.B * p.Hq;
-  const WorkItem wi = work_item(BH, p.n_splits);
+  const WorkItem wi = work_item_of(item, BH, p.n_splits);
   const int32_t bh = xcd_head_swizzle(wi.bh, BH);
   const int32_t t_lin = wi.t_lin;
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
@@ -685,9 +686,95 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
   if (hl == 0) lse_w[orow] = mw.lse;
 }
 
+// D = 64: 64 KB of LDS and at most 128 registers per wave, two workgroups per
+// compute unit (four waves per SIMD); D = 128: one workgroup, two waves per SIMD.
+template <typename TT, int D, bool OUT_F32, bool BUF>
+__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel(
+    const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
+    const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
+    FwdParams p, Sched s) {
+  fwd_item<TT, D, OUT_F32, BUF>(q, k, v, out, lse, p, s, blockIdx.x);
+}
+
+// The same work items taken from queues instead of one workgroup each: a grid
+// of as many workgroups as the chip holds at once, where every workgroup
+// repeatedly takes the next item of a queue.  Queue j (a counter in `queues`,
+// zero at launch) hands out items j, j + 8, j + 16, ... in that order: the
+// items a one-per-workgroup launch would run on XCD j (workgroups are dealt
+// to the 8 XCDs round-robin), so each XCD keeps streaming the same heads'
+// keys and values through its L2.  A workgroup serves its own XCD's queue
+// and, once that is empty, takes the remaining items of the others: XCDs
+// that run at a higher clock take on more of the work instead of idling at
+// the end.  Every item is taken exactly once (each ticket of an atomic
+// counter goes to one workgroup), so the results are those of the
+// one-per-workgroup launch.
+constexpr uint32_t kNoItem = 0xffffffffu;
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 7;
+}
+template <typename TT, int D, bool OUT_F32, bool BUF>
+__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_queue_kernel(
+    const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
+    const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
+    FwdParams p, Sched s, uint32_t* __restrict__ queues, uint32_t n_items) {
+  __shared__ uint32_t next;
+  const uint32_t home = xcc_id();
+  uint32_t skip = 0;  // queues this workgroup found empty (thread 0)
+  for (;;) {
+    if (threadIdx.x == 0) {
+      uint32_t id = kNoItem;
+      for (; skip < 8; ++skip) {
+        const uint32_t j = (home + skip) & 7;
+        const uint64_t cand = j + 8ull * atomicAdd(&queues[j], 1u);
+        if (cand < n_items) {
+          id = (uint32_t)cand;
+          break;
+        }
+      }
+      next = id;
+    }
+    __syncthreads();
+    const uint32_t id = next;
+    __syncthreads();  // every thread has read `next` before thread 0 writes it again
+    if (id == kNoItem) return;
+    fwd_item<TT, D, OUT_F32, BUF>(q, k, v, out, lse, p, s, id);
+  }
+}
+
+__global__ void zero_queues_kernel(uint32_t* __restrict__ queues) {
+  if (threadIdx.x < kFwdQueues) queues[threadIdx.x] = 0;
+}
+
+// Queue launch of kernel `kq` when the chip holds fewer than half of the
+// `blocks` work items at once; returns false (nothing launched) otherwise.
+template <typename KQ, typename E>
+bool launch_queued(KQ kq, int64_t blocks, uint32_t* queues, hipStream_t stream, const E* q,
+                   const E* k, const E* v, void* out, float* lse, const FwdParams& p,
+                   const Sched& s, hipError_t* err) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq, kThreads, 0);
+  if (e != hipSuccess) {
+    *err = e;
+    return true;
+  }
+  if (cus <= 0 || per_cu <= 0) return false;
+  const int64_t grid = (int64_t)cus * per_cu;
+  if (blocks < 2 * grid) return false;
+  hipLaunchKernelGGL(zero_queues_kernel, dim3(1), dim3(64), 0, stream, queues);
+  hipLaunchKernelGGL(kq, dim3((unsigned)grid), dim3(kThreads), 0, stream, q, k, v, out, lse, p,
+                     s, queues, (uint32_t)blocks);
+  *err = hipGetLastError();
+  return true;
+}
+
 template <typename TT, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse,
-                    bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
+                    bool out_f32, const FwdParams& p, const Sched& s, uint32_t* queues,
+                    hipStream_t stream) {
   using E = typename TT::elem;
   const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq * p.n_splits;
   if (blocks <= 0) return hipSuccess;
@@ -696,6 +783,25 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
   const bool buf = (uint64_t)p.Nk * (uint64_t)p.Hkv * D * sizeof(E) <= 0xFFFF0000ull;
   const dim3 g((unsigned)blocks), t(kThreads);
   const E *qe = (const E*)q, *ke = (const E*)k, *ve = (const E*)v;
+  // queued launches at d = 128 only: at d = 64 and 32 the loop around the
+  // item does not fit the register budget of two workgroups per compute unit
+  if constexpr (D == 128) if (queues && blocks <= 0xFFFFFFF0ll) {
+    hipError_t e = hipSuccess;
+    bool done;
+    if (out_f32 && buf)
+      done = launch_queued(fwd_mfma128_queue_kernel<TT, D, true, true>, blocks, queues, stream,
+                           qe, ke, ve, out, lse, p, s, &e);
+    else if (out_f32)
+      done = launch_queued(fwd_mfma128_queue_kernel<TT, D, true, false>, blocks, queues, stream,
+                           qe, ke, ve, out, lse, p, s, &e);
+    else if (buf)
+      done = launch_queued(fwd_mfma128_queue_kernel<TT, D, false, true>, blocks, queues, stream,
+                           qe, ke, ve, out, lse, p, s, &e);
+    else
+      done = launch_queued(fwd_mfma128_queue_kernel<TT, D, false, false>, blocks, queues, stream,
+                           qe, ke, ve, out, lse, p, s, &e);
+    if (done) return e;
+  }
   if (out_f32 && buf)
     hipLaunchKernelGGL((fwd_mfma128_kernel<TT, D, true, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   else if (out_f32)
@@ -711,16 +817,16 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
 
 hipError_t launch_fwd_mfma128(int dtype, int d, const void* q, const void* k, const void* v,
                               void* out, float* lse, bool out_f32, const FwdParams& p,
-                              const Sched& s, hipStream_t stream) {
+                              const Sched& s, uint32_t* queues, hipStream_t stream) {
   if (d == 128) {
-    if (dtype == 1) return launch_t<F16, 128>(q, k, v, out, lse, out_f32, p, s, stream);
-    if (dtype == 2) return launch_t<Bf16, 128>(q, k, v, out, lse, out_f32, p, s, stream);
+    if (dtype == 1) return launch_t<F16, 128>(q, k, v, out, lse, out_f32, p, s, queues, stream);
+    if (dtype == 2) return launch_t<Bf16, 128>(q, k, v, out, lse, out_f32, p, s, queues, stream);
   } else if (d == 64) {
-    if (dtype == 1) return launch_t<F16, 64>(q, k, v, out, lse, out_f32, p, s, stream);
-    if (dtype == 2) return launch_t<Bf16, 64>(q, k, v, out, lse, out_f32, p, s, stream);
+    if (dtype == 1) return launch_t<F16, 64>(q, k, v, out, lse, out_f32, p, s, queues, stream);
+    if (dtype == 2) return launch_t<Bf16, 64>(q, k, v, out, lse, out_f32, p, s, queues, stream);
   } else if (d == 32) {
-    if (dtype == 1) return launch_t<F16, 32>(q, k, v, out, lse, out_f32, p, s, stream);
-    if (dtype == 2) return launch_t<Bf16, 32>(q, k, v, out, lse, out_f32, p, s, stream);
+    if (dtype == 1) return launch_t<F16, 32>(q, k, v, out, lse, out_f32, p, s, queues, stream);
+    if (dtype == 2) return launch_t<Bf16, 32>(q, k, v, out, lse, out_f32, p, s, queues, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -180,14 +180,16 @@ __device__ __forceinline__ TileCursor cursor_at(const Sched& s, int32_t rank, in
 struct WorkItem {
   int32_t bh, t_lin, split;
 };
-__device__ __forceinline__ WorkItem work_item(int32_t BH, int32_t n_splits) {
-  const uint32_t id = blockIdx.x;
+__device__ __forceinline__ WorkItem work_item_of(uint32_t id, int32_t BH, int32_t n_splits) {
   const uint32_t r = id / (uint32_t)BH;
   WorkItem w;
   w.bh = (int32_t)(id % (uint32_t)BH);
   w.t_lin = (int32_t)(r / (uint32_t)n_splits);
   w.split = (int32_t)(r % (uint32_t)n_splits);
   return w;
+}
+__device__ __forceinline__ WorkItem work_item(int32_t BH, int32_t n_splits) {
+  return work_item_of(blockIdx.x, BH, n_splits);
 }
 
 // First live tile of this split and the number of tiles it takes: split s of

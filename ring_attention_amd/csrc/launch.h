@@ -15,16 +15,23 @@ hipError_t launch_fwd_generic(int dtype, int d, const void* q, const void* k, co
                               void* out, float* lse, bool out_f32, const FwdParams& p,
                               const Sched& s, hipStream_t stream);
 
+// Work-item queues of a queued forward launch: one 32-bit counter per XCD.
+constexpr int kFwdQueues = 8;
+
 // 16-bit inputs, d = 32, 64 or 128 (direct-to-LDS tiles, transposing V reads).
+// queues: nullptr, or kFwdQueues counters in device memory that no other
+// launch uses meanwhile; with them, a d = 128 grid larger than twice what the
+// chip holds at once runs as a persistent grid fed from per-XCD queues (the
+// counters are zeroed on `stream` first).
 hipError_t launch_fwd_mfma128(int dtype, int d, const void* q, const void* k, const void* v,
                               void* out, float* lse, bool out_f32, const FwdParams& p,
-                              const Sched& s, hipStream_t stream);
+                              const Sched& s, uint32_t* queues, hipStream_t stream);
 
 // 16-bit inputs, d in {16, 32, 64, 128} (d = 32, 64 and 128 are routed to
-// launch_fwd_mfma128).
+// launch_fwd_mfma128, with `queues`; d = 16 ignores them).
 hipError_t launch_fwd_mfma(int dtype, int d, const void* q, const void* k, const void* v,
                            void* out, float* lse, bool out_f32, const FwdParams& p,
-                           const Sched& s, hipStream_t stream);
+                           const Sched& s, uint32_t* queues, hipStream_t stream);
 
 hipError_t launch_merge(float* out, float* lse, const float* blk_out, const float* blk_lse,
                         int B, int H, int64_t Nq, int64_t Nb, int64_t row_off, int d,

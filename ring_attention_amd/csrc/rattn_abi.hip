@@ -98,11 +98,11 @@ FwdParams make_params(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, float scal
 
 int dispatch(int dtype, int d, const void* q, const void* k, const void* v, void* out,
              float* lse, bool out_f32, const FwdParams& p, const Sched& s, int64_t grid,
-             void* stream) {
+             void* stream, uint32_t* queues = nullptr) {
   if (grid > INT32_MAX) return RATTN_EUNSUPPORTED;
   hipError_t e;
   if (use_mfma(dtype, d))
-    e = launch_fwd_mfma(dtype, d, q, k, v, out, lse, out_f32, p, s, (hipStream_t)stream);
+    e = launch_fwd_mfma(dtype, d, q, k, v, out, lse, out_f32, p, s, queues, (hipStream_t)stream);
   else
     e = launch_fwd_generic(dtype, d, q, k, v, out, lse, out_f32, p, s, (hipStream_t)stream);
   return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
@@ -183,6 +183,22 @@ extern "C" int rattn_fwd(const void* q, const void* k, const void* v, void* out,
   if (rc != RATTN_OK || Nq == 0) return rc;
   const FwdParams p = make_params(B, Hq, Hkv, Nq, N, resolve_scale(scale, d));
   return dispatch(dtype, d, q, k, v, out, lse, false, p, s, (int64_t)s.n_tiles * B * Hq, stream);
+}
+
+extern "C" int rattn_fwd_queued(const void* q, const void* k, const void* v, void* out,
+                                float* lse, int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d,
+                                int dtype, float scale, int causal, int n_ring_steps, int zigzag,
+                                int rank, void* queue_ws, int64_t queue_ws_bytes, void* stream) {
+  Sched s;
+  const int rc = prepare_ring(q, k, v, out, lse, B, Hq, Hkv, Nq, N, d, dtype, causal,
+                              n_ring_steps, zigzag, rank, &s);
+  if (rc != RATTN_OK || Nq == 0) return rc;
+  if (!queue_ws || queue_ws_bytes < RATTN_QUEUE_WS_BYTES || !aligned(queue_ws, 4))
+    return RATTN_EINVAL;
+  static_assert(kFwdQueues * sizeof(uint32_t) <= RATTN_QUEUE_WS_BYTES, "queue workspace");
+  const FwdParams p = make_params(B, Hq, Hkv, Nq, N, resolve_scale(scale, d));
+  return dispatch(dtype, d, q, k, v, out, lse, false, p, s, (int64_t)s.n_tiles * B * Hq, stream,
+                  (uint32_t*)queue_ws);
 }
 
 extern "C" int rattn_fwd_varlen(const void* q, const void* k, const void* v, void* out,
