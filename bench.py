@@ -6,10 +6,12 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 the long-context GQA causal workload (batch 1, 524288 tokens, 32 query heads
 over 8 key/value heads, d = 128, bf16, N(0,1)) processed as the 8-device
 ZigZag ring schedule (16 chunks of 32768) of every device in one launch of
-rattn_fwd: every query tile walks its device's key/value chunks in ring order,
-skips fully masked tiles, masks the diagonal ones, keeps the online softmax
-in registers and merges the ring steps in place (one running max, sum and
-accumulator per row), dividing by the sum once at the end.
+rattn_fwd_queued: every query tile walks its device's key/value chunks in ring
+order, skips fully masked tiles, masks the diagonal ones, keeps the online
+softmax in registers and merges the ring steps in place (one running max, sum
+and accumulator per row), dividing by the sum once at the end; the query
+tiles are handed to a persistent grid from per-XCD queues.  The same
+workload through rattn_fwd (one workgroup per query tile) is an extra.
 
 `value` is causal-adjusted TFLOP/s: 4*d FLOP per visible (query, key) pair
 per query head (2d for QK^T, 2d for PV; exponentials and masked work are not
@@ -42,9 +44,9 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 MFMA_BF16_FLOP_PER_CLK_CU = 4096  # 4 SIMDs x one 32x32x16 bf16 MFMA (32768 FLOP) per 32 clocks
 # the dominant kernel of the headline workload (d = 128, 16-bit, output in the input type)
-HEADLINE_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, false, true>"
+HEADLINE_KERNEL = "rattn::fwd_mfma128_queue_kernel<rattn::Bf16, 128, false, true>"
 # the ring-step kernel (d = 128, 16-bit, float32 partials merged in the epilogue)
-STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, true, true>"
+STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, 128, true, true>"
 # sources the d = 128 kernel is built from; a stored counter summary is valid
 # only for the kernel it was measured on
 KERNEL_SOURCES = ("fwd_mfma128.hip", "kcommon.h", "ring_sched.h", "launch.h")
@@ -345,7 +347,7 @@ def device_peak(torch):
 
 
 def headline(torch, binding, workloads, dev, args):
-    """The long-context GQA causal workload: one rattn_fwd launch per step
+    """The long-context GQA causal workload: one rattn_fwd_queued call per step
     (every device's ZigZag ring schedule), W warm-up steps, K timed steps."""
     w = workloads.workload(HEADLINE_WORKLOAD)
     need = 2 * (w.B * w.Nq * w.Hq * w.d) * 2 + 2 * (w.B * w.N * w.Hkv * w.d) * 2 \
@@ -356,12 +358,14 @@ def headline(torch, binding, workloads, dev, args):
               f"{free / 1e9:.1f} GB are free", file=sys.stderr)
         sys.exit(1)
     q, k, v = workloads.make_inputs(w, device=dev)
+    queue_ws = binding.queue_workspace(dev)
     torch.cuda.synchronize()
     pairs = w.N * (w.N + 1) // 2  # per head: keys 0..i for query i
     flop = 4 * w.d * w.Hq * w.B * pairs
 
     def step():
-        return binding.fwd(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=-1)
+        return binding.fwd_queued(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=-1,
+                                  queue_ws=queue_ws)
 
     for _ in range(args.warmup):
         step()
@@ -376,7 +380,7 @@ def headline(torch, binding, workloads, dev, args):
     ms_per_step = t0.elapsed_time(t1) / args.steps
     # per-launch HIP events around each call on the stream it runs on (torch's
     # current stream, which the binding passes): one launch of the dominant
-    # kernel per step
+    # kernel per step (after a one-wave kernel that zeroes its 8 queue counters)
     kern = Timer(torch)
     for _ in range(args.steps):
         kern(step)
@@ -541,9 +545,10 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "N": w.N, "Hq": w.Hq,
                    "Hkv": w.Hkv, "d": w.d, "causal": True, "ring": w.W, "zigzag": True,
                    "rank": -1,
-                   "mode": "one rattn_fwd launch per step: the ZigZag ring schedule of all "
-                           "8 simulated devices (16 chunks of 32768 tokens), ring steps merged "
-                           "in place by the online softmax",
+                   "mode": "one rattn_fwd_queued call per step: the ZigZag ring schedule of "
+                           "all 8 simulated devices (16 chunks of 32768 tokens), ring steps "
+                           "merged in place by the online softmax, query tiles handed out from "
+                           "per-XCD queues to a persistent grid",
                    "visible_pairs_per_head": pairs,
                    "flop_per_step": flop,
                    # the usual causal estimate, half of all (query, key) pairs
@@ -570,11 +575,24 @@ def main():
     if not args.no_cpu:
         q, k, v = inputs
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_rows)
+    plain = None
+    if not args.no_extras:
+        # the same workload through rattn_fwd: one workgroup per query tile
+        q, k, v = inputs
+
+        def run_plain():
+            return binding.fwd(q, k, v, causal=True, n_ring_steps=w.W, zigzag=True, rank=-1)
+        run_plain()
+        ms = loop_ms(torch, run_plain, 3)
+        plain = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                 "pct_of_peak": round(100 * flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                 "entry_point": "rattn_fwd"}
+        del q, k, v
     del inputs
     torch.cuda.empty_cache()
 
     if not args.no_extras:
-        extras = {}
+        extras = {w.name + "_rattn_fwd": plain}
 
         def workload_extra(idx):
             we = workloads.workload(idx)

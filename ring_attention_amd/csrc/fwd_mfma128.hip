@@ -234,7 +234,7 @@ __device__ __forceinline__ void run_next(RunCursor& c, const RunCursorCtx& x) {
 
 // One work item (a query tile of a (batch, head), or one key split of it):
 // work item `item` of the enumeration work_item_of describes.
-template <typename TT, int D, bool OUT_F32, bool BUF>
+template <typename TT, int D, bool OUT_F32, bool BUF, bool QUEUED>
 __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q,
                                          const typename TT::elem* __restrict__ k,
                                          const typename TT::elem* __restrict__ v,
@@ -555,12 +555,32 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
     float tsum;
     auto exps = [&](float m_use) {
       float rs[4];
+      // D = 128, one workgroup per item: all shifted scores, then all
+      // exponentials, then their uses, so that no use waits on a just-issued
+      // exponential.  It takes 32 more registers, which the D = 64 and 32
+      // budgets do not have, and which cost the queued kernel more (measured)
+      // than the order gains.
+      constexpr bool kSplitExp = D == 128 && !QUEUED;
+      float x[NKB][16];
+      if constexpr (kSplitExp) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[kb][r] = fmaf(sacc[kb][r], p.c, -m_use);
+        __builtin_amdgcn_sched_barrier(0x4);  // only scalar work moves across
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[kb][r] = exp2_fast(x[kb][r]);
+        __builtin_amdgcn_sched_barrier(0x4);
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_fast(fmaf(sacc[kb][r], p.c, -m_use));
-          const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], p.c, -m_use));
+          const float p0 = kSplitExp ? x[kb][r] : exp2_fast(fmaf(sacc[kb][r], p.c, -m_use));
+          const float p1 =
+              kSplitExp ? x[kb][r + 1] : exp2_fast(fmaf(sacc[kb][r + 1], p.c, -m_use));
           const int i = (r >> 1) & 3;
           rs[i] = (kb == 0 && r < 8) ? p0 : rs[i] + p0;
           rs[i] += p1;
@@ -693,7 +713,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
     FwdParams p, Sched s) {
-  fwd_item<TT, D, OUT_F32, BUF>(q, k, v, out, lse, p, s, blockIdx.x);
+  fwd_item<TT, D, OUT_F32, BUF, false>(q, k, v, out, lse, p, s, blockIdx.x);
 }
 
 // The same work items taken from queues instead of one workgroup each: a grid
@@ -739,7 +759,7 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_queue_
     const uint32_t id = next;
     __syncthreads();  // every thread has read `next` before thread 0 writes it again
     if (id == kNoItem) return;
-    fwd_item<TT, D, OUT_F32, BUF>(q, k, v, out, lse, p, s, id);
+    fwd_item<TT, D, OUT_F32, BUF, true>(q, k, v, out, lse, p, s, id);
   }
 }
 
