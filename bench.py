@@ -51,7 +51,7 @@ STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, 128, true, true>"
 # only for the kernel it was measured on
 KERNEL_SOURCES = ("fwd_mfma128.hip", "kcommon.h", "ring_sched.h", "launch.h")
 HEADLINE_COUNTERS = os.path.join(ROOT, "profiles",
-                                 "fwd_mfma128_gqa_causal_512k_bf16_hbm_counters.txt")
+                                 "fwd_mfma128_queue_gqa_causal_512k_bf16_hbm_counters.txt")
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles",
                                "fwd_mfma128_zigzag_rank2_131k_bf16_hbm_counters.txt")
 HEADLINE_WORKLOAD = 5
