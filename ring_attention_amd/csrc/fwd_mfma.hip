@@ -12,8 +12,10 @@
 //
 // How, on CDNA4:
 //   * A workgroup of 4 wavefronts owns a tile of 128 query rows, 32 per wave;
-//     d = 16, 32 or 64 (at d = 16 the V^T operand is padded to 32 rows with
-//     zeros and only O^T rows 0..15 are stored).
+//     d = 16 (the V^T operand is padded to 32 rows with zeros and only O^T
+//     rows 0..15 are stored).  Larger d runs on fwd_mfma128.hip's kernel;
+//     the template below is written for any d that is a multiple of 16, and
+//     only d = 16 is instantiated.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_{bf16,f16}: A = 32 keys x 16 dims read from LDS,
 //     B = 16 dims x 32 queries held in registers for the whole tile.  In the
@@ -336,12 +338,8 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
 template <typename TT>
 hipError_t launch_d(int d, const void* q, const void* k, const void* v, void* out, float* lse,
                     bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
-  switch (d) {
-    case 16: return launch_t<TT, 16>(q, k, v, out, lse, out_f32, p, s, stream);
-    case 32: return launch_t<TT, 32>(q, k, v, out, lse, out_f32, p, s, stream);
-    case 64: return launch_t<TT, 64>(q, k, v, out, lse, out_f32, p, s, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (d == 16) return launch_t<TT, 16>(q, k, v, out, lse, out_f32, p, s, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
