@@ -52,27 +52,14 @@ def _direct(kind, fn):
     return fn()
 
 
-def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag: bool,
-                       rank: int, causal: bool = True, scale: float | None = None,
-                       hook=_direct, fused_merge: bool = True):
-    """Run device ``rank``'s W ring steps; returns float32 (out, lse).
-
-    q_shard [B, Nq, Hq, d] is the device's query shard; k_shards[src] and
-    v_shards[src] are the shards every device would send (see ``shard``).
-    fused_merge: steps after the first merge into the running result in the
-    step kernel's epilogue (rattn_fwd_step_merge); else each writes a partial
-    that rattn_merge folds in.  hook(kind, fn) wraps every library call
-    ("step" or "merge") and must return fn(); a benchmark uses it to time
-    the launches.
-    """
-    N = sum(k.shape[1] for k in k_shards)
-    B, Nq, Hq, d = q_shard.shape
-    out = lse = None
+def step_plan(N: int, W: int, zigzag: bool, rank: int, causal: bool):
+    """Device ``rank``'s ring steps in order, skipped steps left out:
+    (src, query runs, key runs, step causal, first query row of the step)."""
     q_runs = shard_rows(N, W, zigzag, rank)
+    plan = []
     for s in range(W):
         src = (rank - s) % W
         k_runs = shard_rows(N, W, zigzag, src)
-        kb, vb = k_shards[src], v_shards[src]
         row_off = 0  # first query row of the step (rows of the shard are read in place)
         qr, kr, step_causal = q_runs, k_runs, causal
         if zigzag and causal:
@@ -87,6 +74,27 @@ def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag
             if src > rank:
                 continue
             step_causal = src == rank
+        plan.append((src, qr, kr, step_causal, row_off))
+    return plan
+
+
+def ring_forward_steps(q_shard: torch.Tensor, k_shards, v_shards, W: int, zigzag: bool,
+                       rank: int, causal: bool = True, scale: float | None = None,
+                       hook=_direct, fused_merge: bool = True):
+    """Run device ``rank``'s W ring steps; returns float32 (out, lse).
+
+    q_shard [B, Nq, Hq, d] is the device's query shard; k_shards[src] and
+    v_shards[src] are the shards every device would send (see ``shard``).
+    fused_merge: steps after the first merge into the running result in the
+    step kernel's epilogue (rattn_fwd_step_merge); else each writes a partial
+    that rattn_merge folds in.  hook(kind, fn) wraps every library call
+    ("step" or "merge") and must return fn(); a benchmark uses it to time
+    the launches.
+    """
+    N = sum(k.shape[1] for k in k_shards)
+    out = lse = None
+    for src, qr, kr, step_causal, row_off in step_plan(N, W, zigzag, rank, causal):
+        kb, vb = k_shards[src], v_shards[src]
         if out is None:
             # the first step writes the running result directly
             out, lse = hook("step", lambda: binding.fwd_step(q_shard, kb, vb, step_causal, qr, kr,
