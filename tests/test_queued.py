@@ -120,3 +120,24 @@ def test_queued_rank_shard(gpu):
     assert same(out, ref_o) and same(lse, ref_l)
     oracle_rows(q, k, v, out, lse, rows_of(B, q.shape[1], Hq, 16, seed=6), pos, True,
                 "queued rank shard")
+
+
+def test_queued_kv_over_4gb(gpu):
+    """The queued kernel's 64-bit-address DMA form: key/value rows of 16
+    heads past 4 GB (N = 32 x 32769 rows, 4.295e9 bytes each for k and v),
+    one contiguous ring rank's 32769 query rows (2064 work items, ragged last
+    tile), causal.  Equal to rattn_fwd bit for bit; sampled rows against the
+    oracle."""
+    W, rank, H, d = 32, 5, 16, 128
+    N = W * 32769
+    assert N * H * d * 2 > 0xFFFF0000
+    note("case queued kv over 4 GB: generating inputs on the GPU")
+    q_all, k, v = workloads.make_qkv(1, 32769, N, H, H, d, torch.bfloat16, seed=35, device=gpu)
+    q = q_all.contiguous()
+    ref_o, ref_l = binding.fwd(q, k, v, causal=True, n_ring_steps=W, zigzag=False, rank=rank)
+    out, lse = binding.fwd_queued(q, k, v, causal=True, n_ring_steps=W, zigzag=False, rank=rank)
+    torch.cuda.synchronize()
+    assert same(out, ref_o) and same(lse, ref_l)
+    pos = np.arange(rank * 32769, (rank + 1) * 32769)
+    oracle_rows(q, k, v, out, lse, rows_of(1, 32769, H, 6, seed=7), pos, True,
+                "queued kv over 4 GB")
