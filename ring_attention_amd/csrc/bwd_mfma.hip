@@ -8,31 +8,35 @@
 // P and dS are rounded to the input type before they enter a matrix product
 // (the forward does the same with P); dP - D is formed in float32.
 //
-// How, on CDNA4 (v_mfma_f32_32x32x16_{bf16,f16}, 4 wavefronts per workgroup):
-//   * dK/dV kernel: a workgroup owns 128 keys, 32 per wave, and streams tiles
-//     of 64 query rows (Q, dO, lse, D) through LDS.  A wave keeps its keys'
-//     K and V rows in registers as the B operand of S = Q K^T and
-//     dP = dO V^T, whose 32x32 accumulators give each lane one key column and
-//     16 query rows; P and dS then go straight from those registers into the
-//     B operand of dV^T += dO^T P and dK^T += Q^T dS, with the A operands
-//     dO^T and Q^T read by transposing LDS reads (ds_read_b64_tr_b16).  The
-//     query rows of every head of the key/value head's GQA group are
-//     streamed in turn, so dK and dV need no reduction across workgroups.
-//   * dQ kernel: a workgroup owns 128 query rows (Q, dO in registers) and
+// How, on CDNA4 (v_mfma_f32_32x32x16_{bf16,f16}, 8 wavefronts per workgroup):
+//   * dK/dV kernel: a workgroup owns 128 keys; their K and V rows sit in LDS
+//     and are the B operand of S = Q K^T and dP = dO V^T, whose 32x32
+//     accumulators give each lane one key column and 16 query rows.  Tiles of
+//     64 query rows (Q, dO, lse, D) stream through LDS; P and dS go straight
+//     from the accumulator registers into the B operand of dV^T += dO^T P and
+//     dK^T += Q^T dS, with the A operands dO^T and Q^T read by transposing
+//     LDS reads (ds_read_b64_tr_b16).  The query rows of every head of the
+//     key/value head's GQA group are streamed in turn, so dK and dV need no
+//     reduction across workgroups.
+//   * dQ kernel: a workgroup owns 256 query rows (Q, dO in registers) and
 //     streams tiles of 64 keys (K, V): S^T = K Q^T and dP^T = V dO^T put one
 //     query per lane, so lse and D are one register each; dQ^T += K^T dS^T
-//     with K^T read transposed from the same LDS tile.
-//   * Tiles move global -> LDS by direct-to-LDS DMA (global_load_lds), double
-//     buffered: tile t+1 is requested before the matrix work of tile t and
-//     waited for before the barrier that ends it.  One XOR swizzle serves both
-//     LDS read patterns of a tile: 16-byte chunk c of row r sits at chunk
-//     slot c ^ (4 (r mod 4) + (r div 4) mod 4), so the 16 rows of a row-
-//     fragment read and the 4 rows x 4 chunks of a transposing read land in
-//     distinct banks.
-//   * Causal: the dQ kernel visits the live prefix of key tiles; the dK/dV
-//     kernel starts each query run at the first row that can see its keys.
-//     A wave skips the matrix work of a tile none of its pairs sees; element
-//     masks only on diagonal or ragged tiles.
+//     with K^T read transposed from the same LDS tile.  Its two wave groups
+//     run in ping-pong, as in the forward (see the kernel).
+//   * Tiles move global -> LDS by direct-to-LDS DMA (buffer_load ... lds):
+//     double buffered in the dK/dV kernel, a ring of 4 buffers in the dQ
+//     kernel.  One XOR swizzle serves both LDS read patterns of a tile:
+//     16-byte chunk c of row r sits at chunk slot
+//     c ^ (4 (r mod 4) + (r div 4) mod 4), so the 16 rows of a row-fragment
+//     read and the 4 rows x 4 chunks of a transposing read land in distinct
+//     banks.
+//   * Causal: the dQ kernel visits the live prefix of key tiles (a tile none
+//     of a wave's rows sees gets dS = 0); the dK/dV kernel starts each query
+//     run at the first row that can see its keys and skips the matrix work
+//     of a tile none of a wave's pairs sees.  Element masks only on diagonal
+//     or ragged tiles.
+#include <type_traits>
+
 #include "bwd.h"
 
 namespace rattn {
@@ -43,10 +47,9 @@ constexpr int D = 128;
 constexpr int KS = D / 16;                  // k-steps of a contraction over d
 constexpr int DB = D / 32;                  // 32-row blocks of d
 constexpr int kRowBytes = D * 2;
-constexpr int kThreads = 256;               // 4 wavefronts
 constexpr int kRows = 64;                   // rows of a streamed tile
 constexpr int kTileBytes = kRows * kRowBytes;  // 16 KB
-constexpr int kOwn = 128;                   // rows a workgroup owns (32 per wave)
+constexpr int kOwn = 128;                   // keys a dK/dV workgroup owns (32 per wave)
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -483,31 +486,59 @@ __global__ __launch_bounds__(kThreadsKV, 1) void bwd_dkv_mfma_kernel(
     }
 }
 
-// ---- dQ ----------------------------------------------------------------------
+// ---- dQ, two wave groups in ping-pong -----------------------------------------
+// Eight wavefronts own 256 query rows, 32 per wave (Q and dO rows in
+// registers as the B operands of S^T = K Q^T and dP^T = V dO^T, one query
+// per lane); waves w and w+4 share a SIMD.  Waves 0-3 form group A, waves
+// 4-7 group B.  Per key tile k each group runs an MFMA phase
+// M_k = {dQ^T += K^T dS^T of tile k-1, S^T and dP^T of tile k} (48 MFMAs)
+// and a vector phase V_k = {P = exp2(S c - lse log2 e), mask, dS = P (dP - D),
+// packed to the input type} of tile k.  Group B runs one phase behind group
+// A, so on every SIMD one group's vector work runs next to the other
+// group's matrix work:
+//      window   0  |  1  |   2    |   3    |  ...
+//      A        M0 | V0  | M1  V1 | M2  V2 |
+//      B        -- | M0  | V0  M1 | V1  M2 |
+// with one workgroup barrier per window.  Key tiles (K and V, 64 rows each)
+// move global -> LDS by direct-to-LDS DMA into a ring of 4 buffers; each
+// wave requests its share of tile m at the start of its M phase for tile
+// m-2.  A tile a wave does not see gets dS = 0 (its S and dP are computed
+// and dropped), so that every M phase runs the same MFMA stream.
+constexpr int kPPWaves = 8;
+constexpr int kThreadsPP = 64 * kPPWaves;
+constexpr int kOwnPP = 32 * kPPWaves;  // query rows per workgroup
+constexpr int kNBuf = 4;
+
+__device__ __forceinline__ void wait_dma_but_one_tile4() {
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+__device__ __forceinline__ void slot_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <typename TT, bool ACC, bool BUF>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
+__global__ __launch_bounds__(kThreadsPP, 1) void bwd_dq_pp_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, const typename TT::elem* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, void* __restrict__ dq,
     BwdParams p) {
   using E = typename TT::elem;
   using v8 = typename TT::v8;
-  constexpr int kBufBytes = 2 * kTileBytes;  // K, V
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
+  constexpr int kBufBytes = 2 * kTileBytes;  // K, then V
+  __shared__ __attribute__((aligned(1024))) char smem[kNBuf * kBufBytes];
   const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;  // 0: A, 1: B (one phase behind)
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
   const int32_t BH = p.B * p.Hq;
   int32_t bh;
   int64_t tl;
-  work_order(BH, bwd_q_tiles(p, kOwn), p.causal != 0, &bh, &tl);
+  work_order(BH, bwd_q_tiles(p, kOwnPP), p.causal != 0, &bh, &tl);
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
-  const BwdItem item = bwd_q_item(p, kOwn, tl);
+  const BwdItem item = bwd_q_item(p, kOwnPP, tl);
   if (item.tile.rows <= 0) return;  // varlen: a tile past the end of its sequence
   const BwdTile qt = item.tile;
   const BwdRun kr0 = item.other[0], kr1 = item.other[1];  // scalars, as in the dK/dV kernel
@@ -524,12 +555,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
   v8 qf[KS], gf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    if (q_valid) {
+    if (q_valid) {  // a wave past the tile's last row has no row to read
       qf[ks] = *(const v8*)(q + qrow * D + 16 * ks + 8 * hl);
       gf[ks] = *(const v8*)(dout + qrow * D + 16 * ks + 8 * hl);
     } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = gf[ks][e] = (typename TT::elem)0.f;
+      qf[ks] = gf[ks] = v8{};
     }
   }
   const float l2 = q_valid ? lse2_of(lse[qrow]) : __builtin_inff();
@@ -538,18 +568,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16{};
 
-  // key tiles: the live prefix of every key run
+  // key tiles: the live prefix of every key run (for the workgroup's last row)
   const int64_t nt0 =
       item.n_other > 0 ? live_tiles(Run{kr0.row0, kr0.len, kr0.pos0}, qhi, p.causal, kRows) : 0;
   const int64_t nt1 =
       item.n_other > 1 ? live_tiles(Run{kr1.row0, kr1.len, kr1.pos0}, qhi, p.causal, kRows) : 0;
-  const int64_t T = nt0 + nt1;
+  const int T = (int)(nt0 + nt1);  // a run holds fewer than 2^31 rows
   struct KT {
-    int64_t row0;
+    int64_t row0;  // flattened row index in [B * k_rows]
     int64_t pos0;
     int rows;
   };
-  auto tile_of = [&](int64_t t) {
+  auto tile_of = [&](int t) {
     KT x;
     const bool second = t >= nt0;
     const int64_t tt = second ? t - nt0 : t;
@@ -559,78 +589,186 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(
     x.pos0 = (second ? kr1.pos0 : kr0.pos0) + tt * kRows;
     return x;
   };
-  const int64_t kstride = (int64_t)p.Hkv * D;
-  const v4i krs = BUF ? tensor_rsrc(k) : v4i{}, vrs = BUF ? tensor_rsrc(v) : v4i{};
-  auto issue = [&](int64_t t, int buf) {
-    const KT x = tile_of(t);
-    const uint32_t base = smem_addr + buf * kBufBytes;
-    dma_tile<BUF>(k, krs, (int64_t)hkv * D, x.row0, x.rows, kstride, base, wave, lane);
-    dma_tile<BUF>(v, vrs, (int64_t)hkv * D, x.row0, x.rows, kstride, base + kTileBytes, wave,
-                  lane);
-  };
 
-  const FragOff fo = frag_offsets(lane);
-  auto compute = [&](int64_t t, int buf) {
-    const KT x = tile_of(t);
-    const char* kb_l = smem + buf * kBufBytes;
-    const char* vb_l = kb_l + kTileBytes;
-    if (wqrows == 0) return;
-    if (p.causal && x.pos0 > wqhi) return;  // every key of the tile is after the wave's queries
-    const bool need_mask = x.rows < kRows || (p.causal && x.pos0 + x.rows - 1 > wqlo);
-    f32x16 s_acc[2], dp_acc[2];
+  // ---- DMA: wave w moves rows 8w .. 8w+7 of a tile's K and of its V ---------
+  const int64_t kstride = (int64_t)p.Hkv * D;
+  const uint32_t row_bytes = (uint32_t)(kstride * (int64_t)sizeof(E));
+  const v4i krs = BUF ? tensor_rsrc(k) : v4i{}, vrs = BUF ? tensor_rsrc(v) : v4i{};
+  int dma_row[2];
+  uint32_t dma_off[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s_acc[kb] = f32x16{};
-      dp_acc[kb] = f32x16{};
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * wave + 4 * i + (lane >> 4);
+    dma_row[i] = r;
+    dma_off[i] = (uint32_t)r * row_bytes + 16 * ((lane & 15) ^ swz(r));
+  }
+  int n_req = 0;
+  // request the next tile (none once all T are requested); rows past the
+  // end of a ragged tile repeat its last row (finite; their dS is 0)
+  auto issue_next = [&]() {
+    if (n_req >= T) return;
+    const KT x = tile_of(n_req);
+    const uint32_t lds = smem_addr + (n_req & (kNBuf - 1)) * kBufBytes + 8 * wave * kRowBytes;
+    ++n_req;
+    const int64_t tb = (x.row0 * kstride + (int64_t)hkv * D) * (int64_t)sizeof(E);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s_acc[kb] = TT::mfma32x32x16(row_frag<TT>(kb_l, fo, ks, kb), qf[ks], s_acc[kb]);
-        dp_acc[kb] = TT::mfma32x32x16(row_frag<TT>(vb_l, fo, ks, kb), gf[ks], dp_acc[kb]);
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t back =
+          dma_row[i] > x.rows - 1 ? (uint32_t)(dma_row[i] - (x.rows - 1)) * row_bytes : 0u;
+      const uint32_t lk = lds + 4 * i * kRowBytes;
+      if (BUF) {
+        dma16(krs, (uint32_t)tb, dma_off[i] - back, lk);
+        dma16(vrs, (uint32_t)tb, dma_off[i] - back, lk + kTileBytes);
+      } else {
+        dma16((const char*)k + tb + (dma_off[i] - back), lk);
+        dma16((const char*)v + tb + (dma_off[i] - back), lk + kTileBytes);
       }
     }
+  };
+  // Group B's first M phase runs the full MFMA stream, so its dQ reads the K
+  // half of buffer kNBuf-1 with dS = 0: zero it so that 0 * K stays 0 (no
+  // DMA targets that buffer before both groups' first M phase).
+  {
+    uint4* z = (uint4*)(smem + (kNBuf - 1) * kBufBytes);
+    for (int i = tid; i < kTileBytes / 16; i += kThreadsPP) z[i] = uint4{0, 0, 0, 0};
+  }
+  issue_next();  // tile 0
+  issue_next();  // tile 1
+  if (T > 1) wait_dma_but_one_tile4(); else wait_dma();
+  __syncthreads();
+
+  const FragOff fo = frag_offsets(lane);
+  f32x16 sacc[2], dpacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) sacc[kb] = dpacc[kb] = f32x16{};
+  float dw[16];  // dS of the last scored tile, packed (key pair (r, r+1) of block kb -> 8 kb + r/2)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dw[i] = 0.f;
+
+  // One M phase as a flat stream: dQ (16 MFMAs, u-major, db-minor), then S
+  // and dP (16 + 16, ks-major: S kb 0, S kb 1, dP kb 0, dP kb 1).  Each
+  // MFMA's LDS operand is read kAhead MFMAs ahead.
+  constexpr int kAhead = 3;
+  auto mfma_stream = [&](auto dq_tag, auto sp_tag, const char* dqb, const char* spb) {
+    constexpr bool DQ = decltype(dq_tag)::value;
+    constexpr bool SP = decltype(sp_tag)::value;
+    constexpr int NDQ = DQ ? 4 * DB : 0;
+    constexpr int N = NDQ + (SP ? 4 * KS : 0);
+    auto load = [&](int i) -> v8 {
+      if (DQ && i < NDQ) return tr_frag<TT>(dqb, fo, i % DB, i / DB);
+      const int j = i - NDQ;
+      const int sel = j & 3;  // 0, 1: K rows of block 0, 1; 2, 3: V rows
+      return row_frag<TT>(spb + (sel >> 1) * kTileBytes, fo, j >> 2, sel & 1);
+    };
+    v8 fb[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+      if (i < N) fb[i] = load(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const v8 a = fb[i % kAhead];
+      if (i + kAhead < N) fb[i % kAhead] = load(i + kAhead);
+      if (DQ && i < NDQ) {
+        const int u = i / DB;
+        dqa[i % DB] = TT::mfma32x32x16(a, packed_operand<TT>(dw, u), dqa[i % DB]);
+      } else {
+        const int j = i - NDQ, sel = j & 3, ks = j >> 2;
+        if (sel < 2)
+          sacc[sel] = TT::mfma32x32x16(a, qf[ks], ks == 0 ? f32x16{} : sacc[sel]);
+        else
+          dpacc[sel - 2] = TT::mfma32x32x16(a, gf[ks], ks == 0 ? f32x16{} : dpacc[sel - 2]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep this issue order
+    }
+  };
+  auto m_phase = [&](int kk, auto dq_tag, auto sp_tag) {
+    const char* dqb = smem + ((kk - 1) & (kNBuf - 1)) * kBufBytes;
+    const char* spb = smem + (kk & (kNBuf - 1)) * kBufBytes;
+    __builtin_amdgcn_s_setprio(1);
+    issue_next();
+    mfma_stream(dq_tag, sp_tag, dqb, spb);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+
+  // V phase of tile t: dS into dw (0 for a tile none of the wave's rows sees)
+  int vt = 0;
+  auto v_phase = [&]() {
+    const KT x = tile_of(vt);
+    ++vt;
+    if (wqrows == 0 || (p.causal && x.pos0 > wqhi)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dw[i] = 0.f;
+      return;
+    }
+    const bool need_mask = x.rows < kRows || (p.causal && x.pos0 + x.rows - 1 > wqlo);
     // key of register r of block kb: 32 kb + 8 (r/4) + 4 hl + r%4; keys
     // below lim are visible to this lane's query
     const int lim =
         (need_mask ? visible_limit(x.rows, p.causal, qpos - x.pos0) : kRows) - 4 * hl;
-    // dS of each block, each step over its 16 registers at once so that the
-    // independent chains overlap
-    float dw[16];
+    float pr[2][16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float ds[16];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) ds[rr] = exp2_fast(fmaf(s_acc[kb][rr], p.c, -l2));
-      if (need_mask) {
+      for (int r = 0; r < 16; ++r) pr[kb][r] = fmaf(sacc[kb][r], p.c, -l2);
+    __builtin_amdgcn_sched_barrier(0x4);  // only scalar work moves across
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int kk2 = 32 * kb + 8 * (rr >> 2) + (rr & 3);
-          ds[rr] = kk2 < lim ? ds[rr] : 0.f;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[kb][r] = exp2_fast(pr[kb][r]);
+    __builtin_amdgcn_sched_barrier(0x4);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk2 = 32 * kb + 8 * (r >> 2) + (r & 3);
+          pr[kb][r] = kk2 < lim ? pr[kb][r] : 0.f;
         }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) ds[rr] *= dp_acc[kb][rr] - dl;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) pack_pair<TT>(&dw[8 * kb + (r >> 1)], ds[r], ds[r + 1]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const v8 du = packed_operand<TT>(dw, u);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        dqa[db] = TT::mfma32x32x16(tr_frag<TT>(kb_l, fo, db, u), du, dqa[db]);
-    }
+      for (int r = 0; r < 16; r += 2)
+        pack_pair<TT>(&dw[8 * kb + (r >> 1)], pr[kb][r] * (dpacc[kb][r] - dl),
+                      pr[kb][r + 1] * (dpacc[kb][r + 1] - dl));
   };
 
-  if (T > 0) {
-    issue(0, 0);
-    wait_dma();
-    __syncthreads();
-    for (int64_t t = 0; t < T; ++t) {
-      if (t + 1 < T) issue(t + 1, (int)((t + 1) & 1));
-      compute(t, (int)(t & 1));
-      wait_dma();
-      __syncthreads();
+  // Before the window in which the groups score tile j, tile j must have
+  // landed on every wave; only tile j+1's requests may still be in flight.
+  auto wait_tile = [&](int j) {
+    if (j + 1 < T) wait_dma_but_one_tile4(); else wait_dma();
+  };
+  // Windows as in the forward's ping-pong: buffer m%4 is written (tile m,
+  // window m-1) after the barrier that ends window m-2, where its last
+  // readers (the dQ of tile m-4 in both groups' M_{m-3}) are done; tile m is
+  // complete on every wave at the barrier that ends window m, before its
+  // first reader (M_m, window m+1).  Both groups pass T+1 barriers.
+  if (group == 0) {
+    m_phase(0, no{}, yes{});
+    slot_barrier();
+    for (int j = 0; j + 1 < T; ++j) {
+      v_phase();
+      wait_tile(j + 1);
+      slot_barrier();
+      m_phase(j + 1, yes{}, yes{});
     }
+    if (T > 0) {
+      v_phase();
+      wait_tile(T);
+      slot_barrier();
+      m_phase(T, yes{}, no{});  // dQ of the last tile
+    }
+  } else {
+    slot_barrier();
+    for (int j = 0; j < T; ++j) {
+      m_phase(j, yes{}, yes{});
+      wait_tile(j + 1);
+      slot_barrier();
+      v_phase();
+    }
+    m_phase(T, yes{}, no{});  // dQ of the last tile
   }
 
   if (!q_valid) return;
@@ -663,15 +801,15 @@ hipError_t launch_acc(const void* q, const void* k, const void* v, const void* d
   const uint64_t lim = 0xFFFF0000ull;
   const bool buf = (uint64_t)p.B * p.q_rows * p.Hq * D * sizeof(E) <= lim &&
                    (uint64_t)p.B * p.k_rows * p.Hkv * D * sizeof(E) <= lim;
-  const int64_t qb = bwd_q_tiles(p, kOwn) * p.B * p.Hq;
+  const int64_t qb = bwd_q_tiles(p, kOwnPP) * p.B * p.Hq;
   if (qb > 0) {
     if (buf)
-      hipLaunchKernelGGL((bwd_dq_mfma_kernel<TT, ACC, true>), dim3((unsigned)qb), dim3(kThreads),
-                         0, stream, (const E*)q, (const E*)k, (const E*)v, (const E*)dout, lse,
-                         delta, dq, p);
+      hipLaunchKernelGGL((bwd_dq_pp_kernel<TT, ACC, true>), dim3((unsigned)qb),
+                         dim3(kThreadsPP), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+                         (const E*)dout, lse, delta, dq, p);
     else
-      hipLaunchKernelGGL((bwd_dq_mfma_kernel<TT, ACC, false>), dim3((unsigned)qb),
-                         dim3(kThreads), 0, stream, (const E*)q, (const E*)k, (const E*)v,
+      hipLaunchKernelGGL((bwd_dq_pp_kernel<TT, ACC, false>), dim3((unsigned)qb),
+                         dim3(kThreadsPP), 0, stream, (const E*)q, (const E*)k, (const E*)v,
                          (const E*)dout, lse, delta, dq, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
