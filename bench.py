@@ -49,7 +49,7 @@ HEADLINE_KERNEL = "rattn::fwd_mfma128_queue_kernel<rattn::Bf16, 128, false, true
 STEP_KERNEL = "rattn::fwd_mfma128_kernel<rattn::Bf16, 128, true, true>"
 # sources the d = 128 kernel is built from; a stored counter summary is valid
 # only for the kernel it was measured on
-KERNEL_SOURCES = ("fwd_mfma128.hip", "kcommon.h", "ring_sched.h", "launch.h")
+KERNEL_SOURCES = ("fwd_mfma128.hip", "kcommon.h", "ring_sched.h", "launch.h", "lds_dma.h")
 HEADLINE_COUNTERS = os.path.join(ROOT, "profiles",
                                  "fwd_mfma128_queue_gqa_causal_512k_bf16_hbm_counters.txt")
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles",

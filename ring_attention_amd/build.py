@@ -22,7 +22,7 @@ OBJ = os.path.join(ROOT, "_build", "rattn")
 LIB = os.path.join(PKG, "librattn.so")
 ARCH = os.environ.get("RATTN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["rattn_abi.hip", "fwd_generic.hip", "fwd_mfma.hip", "fwd_mfma128.hip", "merge.hip",
+SOURCES = ["rattn_abi.hip", "fwd_generic.hip", "fwd_mfma.hip", "fwd_mfma128.hip", "fwd_short.hip", "merge.hip",
            "bwd_generic.hip", "bwd_mfma.hip"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

@@ -2,6 +2,7 @@
 // scheduler that turns (W, zigzag, rank) or explicit segments into query
 // segments and key/value visits, and kernel dispatch.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -96,11 +97,62 @@ FwdParams make_params(int B, int Hq, int Hkv, int64_t Nq, int64_t Nk, float scal
   return p;
 }
 
+// The schedule with query tiles of br rows (same segments, same order).
+bool retile(Sched& s, int br) {
+  int64_t tiles = 0;
+  for (int i = 0; i < s.n_qseg; ++i) {
+    s.qseg[i].tile_begin = (int32_t)tiles;
+    tiles += (s.qseg[i].len + br - 1) / br;
+    if (tiles > INT32_MAX) return false;
+  }
+  s.n_tiles = (int32_t)tiles;
+  s.br = br;
+  return true;
+}
+
+// A d = 128 launch with few 256-row work items runs on the key-split kernel
+// instead (32 query rows per workgroup, the key tiles divided among its 8
+// waves, merged in LDS).  That kernel moves each key/value byte for 32
+// query rows instead of 256, so it pays only where the 256-row items leave
+// compute units idle: at most a quarter of them busy (uniform items), or
+// half of them for causal items (whose lengths vary, so the 256-row launch
+// waits for its longest), and long enough items (the first query tile,
+// the longest under the causal order, sees at least 24 key tiles of 64).
+// Measured on MI355X, d = 128 bf16: one head of 4096 queries 86 -> 29 us;
+// 8 causal heads of 4096 87 -> 69 us; 8 non-causal heads of 4096 stay on
+// the 256-row kernel (91 against 113 us).
+// The environment variable RATTN_FWD_SHORT overrides the choice for every
+// eligible launch: "0" never takes the key-split kernel, "1" always does.
+bool short_launch(int dtype, int d, const FwdParams& p, const Sched& s) {
+  if (!use_mfma(dtype, d) || d != 128 || p.n_splits != 1 || s.mode == kVisitVarlen) return false;
+  const char* env = getenv("RATTN_FWD_SHORT");
+  if (env && env[0] == '0' && env[1] == 0) return false;
+  if (env && env[0] == '1' && env[1] == 0) return true;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;  // the regular launch reports the error
+  const int64_t items = (int64_t)s.n_tiles * p.B * p.Hq;
+  if (items <= 0 || items * (s.causal ? 2 : 4) > (int64_t)cus) return false;
+  const QTile qt = query_tile(s, 0, s.br);
+  int64_t t64 = 0;
+  for (int32_t v = 0; v < num_visits(s); ++v)
+    t64 += live_tiles(visit(s, qt.rank, v), qt.pos0 + qt.rows - 1, s.causal, 64);
+  return t64 >= 24;
+}
+
 int dispatch(int dtype, int d, const void* q, const void* k, const void* v, void* out,
              float* lse, bool out_f32, const FwdParams& p, const Sched& s, int64_t grid,
              void* stream, uint32_t* queues = nullptr) {
   if (grid > INT32_MAX) return RATTN_EUNSUPPORTED;
   hipError_t e;
+  if (short_launch(dtype, d, p, s)) {
+    Sched s32 = s;
+    if (retile(s32, kShortBr) && (int64_t)s32.n_tiles * p.B * p.Hq <= INT32_MAX) {
+      e = launch_fwd_short(dtype, q, k, v, out, lse, out_f32, p, s32, (hipStream_t)stream);
+      return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
+    }
+  }
   if (use_mfma(dtype, d))
     e = launch_fwd_mfma(dtype, d, q, k, v, out, lse, out_f32, p, s, queues, (hipStream_t)stream);
   else

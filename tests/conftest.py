@@ -16,6 +16,22 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs a gfx950 GPU (runs the HIP kernels)")
+    config.addinivalue_line(
+        "markers", "fwd_short(mode): RATTN_FWD_SHORT for this test ('auto', '0' or '1')")
+
+
+@pytest.fixture(autouse=True)
+def fwd_short_mode(request, monkeypatch):
+    """Which d = 128 forward kernel small launches take.  Tests pin it to the
+    256-row kernel ("0") unless marked fwd_short("auto") or fwd_short("1"),
+    so that small shapes keep exercising that kernel; the library reads
+    RATTN_FWD_SHORT at every call."""
+    m = request.node.get_closest_marker("fwd_short")
+    mode = m.args[0] if m else "0"
+    if mode == "auto":
+        monkeypatch.delenv("RATTN_FWD_SHORT", raising=False)
+    else:
+        monkeypatch.setenv("RATTN_FWD_SHORT", mode)
 
 
 @pytest.fixture(scope="session")
