@@ -80,6 +80,9 @@ def parse():
                     help="run only the causal layout comparison and print its JSON")
     ap.add_argument("--bwd-only", action="store_true",
                     help="run only the backward measurements and print their JSON")
+    ap.add_argument("--single-head-only", action="store_true",
+                    help="only the single-head 4096-token workload through rattn_fwd "
+                         "(the key-split kernel)")
     ap.add_argument("--ring-share-only", action="store_true",
                     help="run only the 131072-token ZigZag ring share (ring steps, fused) "
                          "and print its JSON")
@@ -91,6 +94,8 @@ def parse():
     ap.add_argument("--summarize-kernels", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "SQ_CSV"),
                     help="print per-kernel HBM GB/s and MFMA busy from three rocprofv3 --pmc "
                          "runs (FETCH_SIZE, WRITE_SIZE, SQ counters) and exit")
+    ap.add_argument("--summarize-waits", metavar="SQ_CSV",
+                    help="wave time shares of every library kernel from an SQ wait-counter pass")
     ap.add_argument("--summarize-mfma", metavar="SQ_CSV",
                     help="print MFMA / VALU / LDS utilisation of the step kernel from a "
                          "rocprofv3 --pmc run of the SQ counters and GRBM_GUI_ACTIVE and exit")
@@ -180,10 +185,44 @@ def summarize_mfma(path: str, kernel: str) -> None:
     print(f"mfma_busy_fraction: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.4f}")
     print(f"mfma_issued_tflops: {avg['SQ_INSTS_MFMA'] * 32768 / t / 1e12:.1f}"
           "  (every v_mfma_f32_32x32x16 counted as 32768 FLOP, masked work included)")
-    print(f"valu_active_fraction: {avg['SQ_ACTIVE_INST_VALU'] / simd_cycles:.4f}")
+    # SQ_ACTIVE_INST_VALU counts quad-cycles (4 clocks)
+    print(f"valu_active_fraction: {4 * avg['SQ_ACTIVE_INST_VALU'] / simd_cycles:.4f}")
     print(f"lds_bank_conflict_cycles: {avg['SQ_LDS_BANK_CONFLICT']:.0f}")
     for c in sorted(avg):
         print(f"  {c}: {avg[c]:.6g}")
+
+
+def summarize_waits(path: str) -> None:
+    """Where the waves of each kernel of this library spend their time, from one
+    SQ pass (SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_ANY,
+    SQ_ACTIVE_INST_VALU, SQ_ACTIVE_INST_LDS: quad-cycles summed over waves;
+    GRBM_GUI_ACTIVE summed over the 8 XCDs).  Shares are of resident
+    wave-time; valu_busy and lds_issue are per SIMD-cycle."""
+    per, dur = {}, {}
+    for r in csv.DictReader(open(path)):
+        name = _short_name(r["Kernel_Name"])
+        if not name.startswith("rattn::"):
+            continue
+        key = (name, r["Dispatch_Id"])
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    names = sorted({k[0] for k in per})
+    print(f"{'kernel':56s} {'n':>5s} {'avg_us':>8s} {'GHz':>5s} {'waves/SIMD':>10s} "
+          f"{'wait_any':>8s} {'wait_issue':>10s} {'active':>7s} {'valu_busy':>9s} "
+          f"{'lds_issue':>9s}")
+    for name in names:
+        ks = [k for k in per if k[0] == name]
+        n = len(ks)
+        avg = {c: sum(per[k].get(c, 0.0) for k in ks) / n for c in per[ks[0]]}
+        t = sum(dur[k] for k in ks) / n
+        xcd_cycles = avg["GRBM_GUI_ACTIVE"] / 8
+        simd_cycles = xcd_cycles * 8 * 32 * 4
+        wc = avg["SQ_WAVE_CYCLES"]
+        print(f"{name[:56]:56s} {n:5d} {t * 1e6:8.1f} {xcd_cycles / t / 1e9:5.2f} "
+              f"{4 * wc / simd_cycles:10.2f} {avg['SQ_WAIT_ANY'] / wc:8.3f} "
+              f"{avg['SQ_WAIT_INST_ANY'] / wc:10.3f} {avg['SQ_ACTIVE_INST_ANY'] / wc:7.3f} "
+              f"{4 * avg['SQ_ACTIVE_INST_VALU'] / simd_cycles:9.3f} "
+              f"{4 * avg['SQ_ACTIVE_INST_LDS'] / simd_cycles:9.3f}")
 
 
 def summarize_kernels(fetch_csv: str, write_csv: str, sq_csv: str) -> None:
@@ -489,6 +528,9 @@ def main():
     if args.summarize_kernels:
         summarize_kernels(*args.summarize_kernels)
         return
+    if args.summarize_waits:
+        summarize_waits(args.summarize_waits)
+        return
 
     import torch
 
@@ -521,6 +563,10 @@ def main():
     if args.ring_share_only:
         print(json.dumps({"extras": ring_share_extra(torch, binding, ring, workloads, dev, args,
                                                      None)}), flush=True)
+        return
+    if args.single_head_only:
+        print(json.dumps({"extras": single_head_extra(torch, binding, workloads, dev, args)}),
+              flush=True)
         return
     peak = device_peak(torch)
     w, inputs, flop, pairs, ms_per_step, launch_ms, avg_launch = headline(
@@ -789,6 +835,32 @@ def varlen_extra(torch, binding, workloads, dev, args):
     return {"varlen_16seq_1k_16k_causal_h32kv8_d128_bf16": {
         "ms": round(ms, 4), "tflops": round(tf, 2),
         "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "tokens": N}}
+
+
+def single_head_extra(torch, binding, workloads, dev, args):
+    """The single-head workload (4096 queries and keys, d=128, bf16) through
+    rattn_fwd, which runs it on the key-split kernel: 128 workgroups of 32
+    query rows, each reading the head's whole K and V (2 MB) from L2 once.
+    That read, over the compute units that do it, is what bounds the kernel
+    (about 140 GB/s per compute unit from L2)."""
+    w = workloads.workload(2)
+    q, k, v = workloads.make_inputs(w, device=dev)
+    flop = 4 * w.d * w.Hq * w.B * w.Nq * w.N
+
+    def run():
+        return binding.fwd(q, k, v)
+    warm_up(torch, run, 5)
+    ms = loop_ms(torch, run, max(50, 2 * args.steps))
+    groups = w.B * w.Hq * ((w.Nq + 31) // 32)
+    kv_bytes = 2 * w.N * w.Hkv * w.d * 2
+    return {w.name: {"ms": round(ms, 4), "us": round(ms * 1e3, 2),
+                     "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                     "pct_of_peak": round(100 * flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "kernel": "fwd_short_kernel (32 query rows per workgroup, key tiles split "
+                               "among 8 waves)",
+                     "workgroups": groups,
+                     "l2_to_cu_bytes": groups * kv_bytes,
+                     "l2_to_cu_GBps_per_busy_cu": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}}
 
 
 def small_d_sweep(torch, binding, workloads, dev, args):
