@@ -1,6 +1,7 @@
-// fwd_short.hip -- the d = 128 attention forward for launches with few query
-// rows per head, where 256-row work items leave most compute units idle
-// (a single head of 4096 queries is 16 such items on 256 compute units).
+// fwd_short.hip -- the attention forward (16-bit, d = 32, 64, 128) for
+// launches with few query rows per head, where 256-row work items leave most
+// compute units idle (a single head of 4096 queries is 16 such items on 256
+// compute units).
 //
 // Method (unchanged): online softmax over key tiles with a running max m,
 // running sum l and unnormalised O, P rounded to the input type before PV,
@@ -19,8 +20,8 @@
 // workgroup's LDS, so the launch allocates nothing.
 //
 // Per wave and key tile j: an MFMA phase {PV of tile j-1, QK of tile j}
-// (8 + 8 v_mfma_f32_32x32x16, interleaved so that dependent MFMAs are two
-// apart) and a softmax phase of tile j.  S^T = K Q^T: the K fragments (A
+// (d/16 + d/16 v_mfma_f32_32x32x16, interleaved so that dependent MFMAs are
+// two apart) and a softmax phase of tile j.  S^T = K Q^T: the K fragments (A
 // operand, key row = lane mod 32) come straight from global memory into
 // registers, one tile ahead; Q is the B operand held in registers.
 // O^T = V^T P^T: V tiles move global -> LDS by direct-to-LDS DMA into two
@@ -38,34 +39,52 @@ namespace rattn {
 
 namespace {
 
-constexpr int D = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBr = kShortBr;        // 32 query rows per workgroup
-constexpr int BC = 32;               // keys per tile
-constexpr int kRowBytes = 2 * D;     // 256
-constexpr int kTileBytes = BC * kRowBytes;  // 8 KB: one K or V tile
-constexpr int KS = D / 16;           // 16-dim MFMA steps of QK
-constexpr int DB = D / 32;           // 32-dim output blocks
-constexpr int NU = BC / 16;          // 16-key MFMA steps of PV
-constexpr int kDmaPerTile = kTileBytes / 1024;  // 1 KB requests: 4 rows each
-// merge area: per wave 32 rows of D floats, padded by 4 floats a row
-constexpr int kMergeRow = D + 4;
-constexpr int kKVBytes = kWaves * 2 * kTileBytes;  // one K and one V tile per wave: 128 KB
-constexpr int kMergeBytes = kWaves * kBr * kMergeRow * 4 + 2 * kWaves * kBr * 4;
-constexpr int kSmemBytes = kKVBytes > kMergeBytes ? kKVBytes : kMergeBytes;
-static_assert(kSmemBytes <= 160 * 1024, "LDS of one workgroup");
+constexpr int kBr = kShortBr;  // 32 query rows per workgroup
+constexpr int BC = 32;         // keys per tile
+constexpr int NU = BC / 16;    // 16-key MFMA steps of PV
 static_assert(kBr == 32, "one MFMA column block of queries per wave");
 
-// LDS slot of 16-byte chunk c of row r: K rows at c ^ (r mod 16), V rows at
-// c ^ 4 (r mod 4), so that a 16-lane K fragment read (16 rows, one chunk
-// each) and a 32-lane transposing V read (4 rows x 8 half-chunks) each touch
-// every LDS bank once.
-__device__ __forceinline__ int kslot(int c, int r) { return c ^ (r & 15); }
-__device__ __forceinline__ int vslot(int c, int r) { return c ^ (4 * (r & 3)); }
+// Geometry of head dimension D (128, 64 or 32).  A K or V row is 2 D bytes,
+// D / 8 chunks of 16 bytes; one 1 KB DMA request moves 512 / D rows.
+// Chunk c of row r sits in LDS at slot
+//   K: c ^ (r mod 16) (D = 128),  c ^ ((r / 2) mod 8) (D = 64),  c ^ ((r / 4) mod 4) (D = 32),
+//   V: c ^ 4 (r mod 4) (D = 128), c ^ 4 ((r / 2) mod 2) (D = 64), c (D = 32),
+// so that a 16-lane K fragment read (16 rows, one chunk each) and a 32-lane
+// transposing V read (4 rows x 8 half-chunks) each touch every LDS bank once
+// (the layout of the 256-row kernel).
+template <int D_>
+struct SGeo {
+  static constexpr int D = D_;
+  static_assert(D == 128 || D == 64 || D == 32, "head dimensions of this kernel");
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kTileBytes = BC * kRowBytes;   // one K or V tile: 8, 4, 2 KB
+  static constexpr int KS = D / 16;                   // 16-dim MFMA steps of QK
+  static constexpr int DB = D / 32;                   // 32-dim output blocks
+  static constexpr int kReq = kTileBytes / 1024;      // 1 KB requests per tile
+  static constexpr int kReqRows = 1024 / kRowBytes;   // rows per request
+  // the K swizzle of the row a lane lands in repeats every kPeriod requests
+  // (the V swizzle is the same for every request)
+  static constexpr int kPeriod = D / 32;
+  // merge area: per wave 32 rows of D floats, padded by 4 floats a row
+  static constexpr int kMergeRow = D + 4;
+  static constexpr int kKVBytes = kWaves * 2 * kTileBytes;  // one K and one V tile per wave
+  static constexpr int kMergeBytes = kWaves * kBr * kMergeRow * 4 + 2 * kWaves * kBr * 4;
+  static constexpr int kSmemBytes = kKVBytes > kMergeBytes ? kKVBytes : kMergeBytes;
+  static_assert(kSmemBytes <= 160 * 1024, "LDS of one workgroup");
+  static_assert(KS == NU * DB, "QK and PV steps alternate one for one");
+  __device__ static int kslot(int c, int r) {
+    return D == 128 ? c ^ (r & 15) : (D == 64 ? c ^ ((r >> 1) & 7) : c ^ ((r >> 2) & 3));
+  }
+  __device__ static int vslot(int c, int r) {
+    return D == 128 ? c ^ (4 * (r & 3)) : (D == 64 ? c ^ (4 * ((r >> 1) & 1)) : c);
+  }
+};
 
 // eight waves, two per SIMD: at most 256 registers per wave
-template <typename TT, bool OUT_F32, bool BUF>
+template <typename TT, int D, bool OUT_F32, bool BUF>
 __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
     const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
     const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
@@ -74,8 +93,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
   using v8 = typename TT::v8;
   using v4 = typename TT::v4;
   using E2 = typename TT::v2;
+  using G = SGeo<D>;
+  constexpr int kRowBytes = G::kRowBytes;
+  constexpr int kTileBytes = G::kTileBytes;
+  constexpr int KS = G::KS;
+  constexpr int DB = G::DB;
 
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[G::kSmemBytes];
   const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
   const int tid = threadIdx.x;
@@ -119,16 +143,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
   const uint32_t row_bytes = (uint32_t)(kv_stride * sizeof(E));
   const v4i krs = BUF ? head_rsrc(kbase) : v4i{}, vrs = BUF ? head_rsrc(vbase) : v4i{};
 
-  // DMA: request j of a tile moves rows 4j .. 4j+3 (1 KB); lane l lands in
-  // slot l mod 16 of row 4j + l/16 and so reads the source chunk stored
-  // there (each swizzle is its own inverse).  Row mod 4 is l/16 for every j,
-  // and row mod 16 repeats after j = 3, so four lane offsets serve K.
-  const int dma_r = lane >> 4;
-  uint32_t k_lane[4];
+  // DMA: request j of a tile moves rows R j .. R j + R-1 (1 KB, R = 512 / D);
+  // lane l lands in slot l mod (D/8) of row R j + l / (D/8) and so reads the
+  // source chunk stored there (each swizzle is its own inverse).  The rows'
+  // offsets go in the scalar offset; the lane parts repeat every kPeriod
+  // requests (K) or not at all (V).
+  const int dma_r = lane / G::kChunks;
+  const int dma_c = lane % G::kChunks;
+  uint32_t k_lane[G::kPeriod];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    k_lane[j] = (uint32_t)(4 * j + dma_r) * row_bytes + 16 * kslot(l16, 4 * j + dma_r);
-  const uint32_t v_lane = (uint32_t)dma_r * row_bytes + 16 * vslot(l16, dma_r);
+  for (int j = 0; j < G::kPeriod; ++j) {
+    const int r = G::kReqRows * j + dma_r;
+    k_lane[j] = (uint32_t)r * row_bytes + 16 * G::kslot(dma_c, r);
+  }
+  const uint32_t v_lane = (uint32_t)dma_r * row_bytes + 16 * G::vslot(dma_c, dma_r);
   const uint32_t kreg = smem_addr + (uint32_t)wave * 2 * kTileBytes;  // this wave's K buffer
   const uint32_t vreg = kreg + kTileBytes;                             // and its V buffer
   const char* kb_ptr = smem + (kreg - smem_addr);
@@ -138,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
   // V^T by transposing reads (16-key step u adds 16 rows)
   uint32_t k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = (uint32_t)(l32 * kRowBytes + 16 * kslot(2 * ks + hl, l32));
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = (uint32_t)(l32 * kRowBytes + 16 * G::kslot(2 * ks + hl, l32));
   uint32_t v_off[DB];
   {
     const int qrow = l16 >> 2;
@@ -147,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
     const int half = (l16 & 1) * 8;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      v_off[db] = (uint32_t)((4 * hl + qrow) * kRowBytes + 16 * vslot(4 * db + c_in, 4 * hl + qrow) +
+      v_off[db] = (uint32_t)((4 * hl + qrow) * kRowBytes + 16 * G::vslot(4 * db + c_in, 4 * hl + qrow) +
                              half);
   }
 
@@ -174,24 +202,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
     const uint32_t dst = is_v ? vreg : kreg;
     const int64_t tb = t.krow0 * (int64_t)row_bytes;
 #pragma unroll
-    for (int j = 0; j < kDmaPerTile; ++j) {
-      // lane offset of row 4j + l/16 relative to the first row of the tile
-      const uint32_t lane_off = is_v ? v_lane + (uint32_t)(4 * j) * row_bytes
-                                     : k_lane[j & 3] + (uint32_t)(16 * (j >> 2)) * row_bytes;
+    for (int j = 0; j < G::kReq; ++j) {
+      // rows of request j before the lane's own: in the scalar offset
+      const uint32_t rows_k = (uint32_t)(G::kReqRows * G::kPeriod * (j / G::kPeriod)) * row_bytes;
+      const uint32_t rows_v = (uint32_t)(G::kReqRows * j) * row_bytes;
+      const uint32_t lane_part = is_v ? v_lane : k_lane[j % G::kPeriod];
+      const uint32_t rows_part = is_v ? rows_v : rows_k;
       if (BUF && t.rows == BC) {
-        // full tile: the rows in the scalar offset where they are uniform
-        const uint32_t so = (uint32_t)tb + (is_v ? (uint32_t)(4 * j) * row_bytes
-                                                 : (uint32_t)(16 * (j >> 2)) * row_bytes);
-        const uint32_t vo = is_v ? v_lane : k_lane[j & 3];
-        dma16(is_v ? vrs : krs, so, vo, dst + 1024 * j);
+        dma16(is_v ? vrs : krs, (uint32_t)tb + rows_part, lane_part, dst + 1024 * j);
         continue;
       }
-      const int r = 4 * j + dma_r;
+      // ragged tile: rows past the end repeat the last one
+      const int r = G::kReqRows * j + dma_r;
       const uint32_t back = r > t.rows - 1 ? (uint32_t)(r - (t.rows - 1)) * row_bytes : 0u;
+      const uint32_t lane_off = rows_part + lane_part - back;
       if (BUF)
-        dma16(is_v ? vrs : krs, (uint32_t)tb, lane_off - back, dst + 1024 * j);
+        dma16(is_v ? vrs : krs, (uint32_t)tb, lane_off, dst + 1024 * j);
       else
-        dma16((is_v ? vbase : kbase) + tb + (lane_off - back), dst + 1024 * j);
+        dma16((is_v ? vbase : kbase) + tb + lane_off, dst + 1024 * j);
     }
   };
 
@@ -229,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
     }
     refill();  // waits for the reads above (lgkmcnt), then DMA into both buffers
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < KS; ++i) {
       if constexpr (QK) sacc = TT::mfma32x32x16(kfr[i], qf[i], i == 0 ? f32x16{} : sacc);
       if constexpr (PV) {
         const int u = i / DB;
@@ -335,6 +363,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
   const float l_tot = pair_sum(l_run);
   __syncthreads();  // every wave is done with its V buffers
   float* mo = (float*)smem;
+  constexpr int kMergeRow = G::kMergeRow;
   float* mm = mo + kWaves * kBr * kMergeRow;
   float* ml = mm + kWaves * kBr;
 #pragma unroll
@@ -353,10 +382,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
   }
   __syncthreads();
 
-  // thread t: row t / 16, dims 8 (t mod 16) .. +7
-  const int row = tid >> 4;
-  const int c8 = (tid & 15) * 8;
-  if (row >= qt.rows) return;
+  // thread t: row t / (D/8), dims 8 (t mod (D/8)) .. +7
+  constexpr int TPR = D / 8;  // threads per row, all in one wave
+  const int row = tid / TPR;
+  const int c8 = (tid % TPR) * 8;
+  if (row >= kBr || row >= qt.rows) return;
   float mx = kNegInf;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, mm[w * kBr + row]);
@@ -406,19 +436,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
     }
     dst[0] = r0;
     dst[1] = r1;
-    // the 16 threads of a row are in one wave, which read the previous lse
+    // the threads of a row are in one wave, which read the previous lse
     // (above, in program order) before this store replaces it
-    if ((tid & 15) == 0) lse[orow] = mw.lse;
+    if (tid % TPR == 0) lse[orow] = mw.lse;
   } else {
     v8 o8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o8[e] = to_elem<TT>(o[e] * inv);
     *(v8*)((E*)out + orow * D + c8) = o8;
-    if ((tid & 15) == 0) lse[orow] = lse_n;
+    if (tid % TPR == 0) lse[orow] = lse_n;
   }
 }
 
-template <typename TT>
+template <typename TT, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse,
                     bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
   using E = typename TT::elem;
@@ -428,23 +458,32 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
   const dim3 g((unsigned)blocks), t(kThreads);
   const E *qe = (const E*)q, *ke = (const E*)k, *ve = (const E*)v;
   if (out_f32 && buf)
-    hipLaunchKernelGGL((fwd_short_kernel<TT, true, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_short_kernel<TT, D, true, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   else if (out_f32)
-    hipLaunchKernelGGL((fwd_short_kernel<TT, true, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_short_kernel<TT, D, true, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   else if (buf)
-    hipLaunchKernelGGL((fwd_short_kernel<TT, false, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_short_kernel<TT, D, false, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   else
-    hipLaunchKernelGGL((fwd_short_kernel<TT, false, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    hipLaunchKernelGGL((fwd_short_kernel<TT, D, false, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
   return hipGetLastError();
+}
+
+template <typename TT>
+hipError_t launch_d(int d, const void* q, const void* k, const void* v, void* out, float* lse,
+                    bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
+  if (d == 128) return launch_t<TT, 128>(q, k, v, out, lse, out_f32, p, s, stream);
+  if (d == 64) return launch_t<TT, 64>(q, k, v, out, lse, out_f32, p, s, stream);
+  if (d == 32) return launch_t<TT, 32>(q, k, v, out, lse, out_f32, p, s, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_short(int dtype, const void* q, const void* k, const void* v, void* out,
-                            float* lse, bool out_f32, const FwdParams& p, const Sched& s,
-                            hipStream_t stream) {
-  if (dtype == 1) return launch_t<F16>(q, k, v, out, lse, out_f32, p, s, stream);
-  if (dtype == 2) return launch_t<Bf16>(q, k, v, out, lse, out_f32, p, s, stream);
+hipError_t launch_fwd_short(int dtype, int d, const void* q, const void* k, const void* v,
+                            void* out, float* lse, bool out_f32, const FwdParams& p,
+                            const Sched& s, hipStream_t stream) {
+  if (dtype == 1) return launch_d<F16>(d, q, k, v, out, lse, out_f32, p, s, stream);
+  if (dtype == 2) return launch_d<Bf16>(d, q, k, v, out, lse, out_f32, p, s, stream);
   return hipErrorInvalidValue;
 }
 

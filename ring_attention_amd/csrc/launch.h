@@ -10,7 +10,7 @@ namespace rattn {
 constexpr int kGenericBr = 64;
 constexpr int kMfmaBr = 128;     // fwd_mfma (16-bit, d = 16)
 constexpr int kMfma128Br = 256;  // fwd_mfma128 (16-bit, d = 32, 64, 128)
-constexpr int kShortBr = 32;     // fwd_short (16-bit, d = 128, few query rows)
+constexpr int kShortBr = 32;     // fwd_short (16-bit, d = 32, 64, 128, few query rows)
 
 hipError_t launch_fwd_generic(int dtype, int d, const void* q, const void* k, const void* v,
                               void* out, float* lse, bool out_f32, const FwdParams& p,
@@ -34,12 +34,12 @@ hipError_t launch_fwd_mfma(int dtype, int d, const void* q, const void* k, const
                            void* out, float* lse, bool out_f32, const FwdParams& p,
                            const Sched& s, uint32_t* queues, hipStream_t stream);
 
-// 16-bit inputs, d = 128, schedule built for kShortBr-row query tiles: one
-// workgroup per tile, whose 8 waves split the tile's key tiles and merge
-// their partial results in LDS (for launches with few query rows).
-hipError_t launch_fwd_short(int dtype, const void* q, const void* k, const void* v, void* out,
-                            float* lse, bool out_f32, const FwdParams& p, const Sched& s,
-                            hipStream_t stream);
+// 16-bit inputs, d = 32, 64 or 128, schedule built for kShortBr-row query
+// tiles: one workgroup per tile, whose 8 waves split the tile's key tiles and
+// merge their partial results in LDS (for launches with few query rows).
+hipError_t launch_fwd_short(int dtype, int d, const void* q, const void* k, const void* v,
+                            void* out, float* lse, bool out_f32, const FwdParams& p,
+                            const Sched& s, hipStream_t stream);
 
 hipError_t launch_merge(float* out, float* lse, const float* blk_out, const float* blk_lse,
                         int B, int H, int64_t Nq, int64_t Nb, int64_t row_off, int d,

@@ -110,21 +110,26 @@ bool retile(Sched& s, int br) {
   return true;
 }
 
-// A d = 128 launch with few 256-row work items runs on the key-split kernel
-// instead (32 query rows per workgroup, the key tiles divided among its 8
-// waves, merged in LDS).  That kernel moves each key/value byte for 32
-// query rows instead of 256, so it pays only where the 256-row items leave
-// compute units idle: at most a quarter of them busy (uniform items), or
-// half of them for causal items (whose lengths vary, so the 256-row launch
-// waits for its longest), and long enough items (the first query tile,
-// the longest under the causal order, sees at least 24 key tiles of 64).
-// Measured on MI355X, d = 128 bf16: one head of 4096 queries 86 -> 29 us;
-// 8 causal heads of 4096 87 -> 69 us; 8 non-causal heads of 4096 stay on
-// the 256-row kernel (91 against 113 us).
+// A 16-bit launch (d = 32, 64, 128) with few 256-row work items runs on the
+// key-split kernel instead (32 query rows per workgroup, the key tiles
+// divided among its 8 waves, merged in LDS).  That kernel moves each
+// key/value byte for 32 query rows instead of 256, so it pays only where the
+// 256-row items leave compute units idle.  Chosen when the items number at
+// most a quarter of the compute units (uniform items), or half of them for
+// causal items (whose lengths vary, so the 256-row launch waits for its
+// longest) -- at d = 32 twice that, the narrow rows costing the key-split
+// kernel less -- and when its items are long (the first query tile, the
+// longest under the causal order, sees at least 24 key tiles of 64) or very
+// few (at most a quarter of the compute units either way).
+// Measured on MI355X (us per call, 256-row kernel -> key-split kernel):
+// d = 128 bf16, one head of 4096 queries 86 -> 29, 8 causal heads of 4096
+// 87 -> 69; 8 non-causal heads of 4096 stay on the 256-row kernel (93 against
+// 117); d = 64 fp16 one head 64 -> 20, (B, N, H) = (2, 1024, 4) 22 -> 13;
+// d = 32 one head 67 -> 15, 16 non-causal heads of 2048 39 -> 29.
 // The environment variable RATTN_FWD_SHORT overrides the choice for every
 // eligible launch: "0" never takes the key-split kernel, "1" always does.
 bool short_launch(int dtype, int d, const FwdParams& p, const Sched& s) {
-  if (!use_mfma(dtype, d) || d != 128 || p.n_splits != 1 || s.mode == kVisitVarlen) return false;
+  if (!use_mfma(dtype, d) || d < 32 || p.n_splits != 1 || s.mode == kVisitVarlen) return false;
   const char* env = getenv("RATTN_FWD_SHORT");
   if (env && env[0] == '0' && env[1] == 0) return false;
   if (env && env[0] == '1' && env[1] == 0) return true;
@@ -133,7 +138,9 @@ bool short_launch(int dtype, int d, const FwdParams& p, const Sched& s) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return false;  // the regular launch reports the error
   const int64_t items = (int64_t)s.n_tiles * p.B * p.Hq;
-  if (items <= 0 || items * (s.causal ? 2 : 4) > (int64_t)cus) return false;
+  const int64_t room = (int64_t)cus * (d == 32 ? 2 : 1);
+  if (items <= 0 || items * (s.causal ? 2 : 4) > room) return false;
+  if (items * 4 <= (int64_t)cus) return true;
   const QTile qt = query_tile(s, 0, s.br);
   int64_t t64 = 0;
   for (int32_t v = 0; v < num_visits(s); ++v)
@@ -149,7 +156,7 @@ int dispatch(int dtype, int d, const void* q, const void* k, const void* v, void
   if (short_launch(dtype, d, p, s)) {
     Sched s32 = s;
     if (retile(s32, kShortBr) && (int64_t)s32.n_tiles * p.B * p.Hq <= INT32_MAX) {
-      e = launch_fwd_short(dtype, q, k, v, out, lse, out_f32, p, s32, (hipStream_t)stream);
+      e = launch_fwd_short(dtype, d, q, k, v, out, lse, out_f32, p, s32, (hipStream_t)stream);
       return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
     }
   }

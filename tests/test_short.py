@@ -1,4 +1,5 @@
-"""The key-split d = 128 forward (fwd_short.hip) vs the fp64 oracle (needs a GPU).
+"""The key-split forward (fwd_short.hip; 16-bit, d = 128, 64, 32) vs the fp64
+oracle (needs a GPU).
 
 Launches whose 256-row work items would occupy at most half of the compute
 units (a single head of 4096 queries: 16 items) run on a kernel that gives
@@ -57,6 +58,35 @@ def test_shapes(gpu, B, N, Hq, Hkv, dtype, causal):
     q, k, v = workloads.make_qkv(B, N, N, Hq, Hkv, 128, dtype, seed=N + 7 * Hq + causal)
     tp.run_full_check(q, k, v, causal, 1, False, -1,
                       f"short B={B} N={N} H={Hq}/{Hkv} {dtype} causal={causal}")
+
+
+# d = 64 and 32: the same kernel with narrower rows (other swizzles, 4 or 2
+# DMA requests per K or V tile, fewer MFMA steps)
+SHAPES_SMALL_D = [(1, 1, 1, 1), (1, 33, 2, 1), (1, 100, 1, 1), (2, 1000, 4, 2), (1, 1500, 8, 2)]
+
+
+@pytest.mark.fwd_short("1")
+@pytest.mark.parametrize("B,N,Hq,Hkv", SHAPES_SMALL_D)
+@pytest.mark.parametrize("d", [64, 32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes_small_d(gpu, B, N, Hq, Hkv, d, dtype, causal):
+    q, k, v = workloads.make_qkv(B, N, N, Hq, Hkv, d, dtype, seed=N + 3 * d + causal)
+    tp.run_full_check(q, k, v, causal, 1, False, -1,
+                      f"short d={d} B={B} N={N} H={Hq}/{Hkv} {dtype} causal={causal}")
+
+
+@pytest.mark.fwd_short("1")
+@pytest.mark.parametrize("d", [64, 32])
+def test_small_d_steps_and_rescaling(gpu, d):
+    """Ring steps (fused and separate merges), large scores and the running-max
+    thresholds at d = 64 and 32."""
+    tp.test_ring_steps_batched_read_shards_in_place(gpu, torch.float16, d, True)
+    tp.test_ring_steps_batched_read_shards_in_place(gpu, torch.bfloat16, d, False)
+    for dtype in (torch.bfloat16, torch.float16):
+        tre.test_large_magnitude_scores(gpu, dtype, d)
+        tre.test_max_moves_every_key_tile(gpu, dtype, d)
+        tre.test_thresholds_of_lazy_rescaling(gpu, dtype, d)
 
 
 @pytest.mark.fwd_short("1")
@@ -142,3 +172,15 @@ def test_auto_choice_matches_forced(gpu):
     assert torch.equal(a_o, f_o) and torch.equal(a_l, f_l)
     ref_o, ref_l = oracle.attention(q.cpu(), k.cpu(), v.cpu(), causal=True)
     tp.compare(tp.host(a_o), tp.host(a_l), ref_o, ref_l, torch.bfloat16, what="auto 2048 causal")
+
+
+@pytest.mark.fwd_short("auto")
+def test_queued_small_launch_matches_fwd(gpu):
+    """rattn_fwd_queued on a launch this small takes the same kernel as
+    rattn_fwd (the queues serve only large launches): equal bit for bit."""
+    q, k, v = workloads.make_qkv(1, 4096, 4096, 2, 2, 128, torch.bfloat16, seed=96, device=gpu)
+    ws = binding.queue_workspace(gpu)
+    a_o, a_l = binding.fwd(q, k, v, causal=True)
+    b_o, b_l = binding.fwd_queued(q, k, v, causal=True, queue_ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a_o, b_o) and torch.equal(a_l, b_l)
