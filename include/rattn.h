@@ -76,10 +76,11 @@ typedef enum { RATTN_F32 = 0, RATTN_F16 = 1, RATTN_BF16 = 2 } rattn_dtype;
  * N must be a multiple of W (of 2W with zigzag).  out has q's dtype.
  * Without causal masking the result does not depend on W, zigzag or rank.
  *
- * Kernel choice (16-bit inputs, d = 128): the work items are query tiles of
- * 256 rows.  When there are few of them (at most a quarter of the compute
- * units, or half of them for causal calls, and the longest item sees at
- * least 24 key tiles of 64), the call runs instead on a kernel that gives
+ * Kernel choice (16-bit inputs, d = 32, 64, 128): the work items are query
+ * tiles of 256 rows.  When there are few of them (at most a quarter of the
+ * compute units, or half of them for causal calls, twice that at d = 32;
+ * beyond a quarter only if the longest item sees at least 24 key tiles of
+ * 64), the call runs instead on a kernel that gives
  * each workgroup 32 query rows and divides their key tiles among its 8
  * waves, whose partial results are merged in LDS by the log-sum-exp rule
  * (for a single head of 4096 queries: 128 workgroups instead of 16).  It
