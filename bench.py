@@ -496,9 +496,28 @@ def ring_share_extra(torch, binding, ring, workloads, dev, args, peak):
     return {w.name: res}
 
 
+def device_us(torch, fn, reps=21):
+    """Median device time of one call in microseconds: the stream is first
+    kept busy by a spin kernel, so the event pair around the call times the
+    GPU work (and the gap between its launches), not the host's enqueueing."""
+    times = []
+    for _ in range(reps):
+        torch.cuda._sleep(1_000_000)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    return sorted(times)[len(times) // 2]
+
+
 def tiny_latency_extra(torch, binding, workloads, dev, args):
     """The 4-device x 8-token ring simulation (fp32, d = 16): latency of one
-    rattn_fwd call in microseconds (back-to-back calls under one event pair)."""
+    rattn_fwd call in microseconds -- per call of back-to-back calls under one
+    event pair (bounded by the host's Python and allocation overhead), and
+    the device time of one call."""
     w = workloads.workload(1)
     q, k, v = workloads.make_inputs(w, device=dev)
 
@@ -507,7 +526,29 @@ def tiny_latency_extra(torch, binding, workloads, dev, args):
     warm_up(torch, run, 10)
     ms = loop_ms(torch, run, 200)
     return {w.name: {"us_per_call": round(ms * 1e3, 2),
+                     "device_us": round(device_us(torch, run), 2),
                      "note": "latency bound: 32 query rows, one workgroup"}}
+
+
+def page_benchmark_sweep(torch, binding, workloads, dev, args):
+    """The shapes of the yz520gzy chapter's attention benchmark (B = 2,
+    H = 32, D = 128, fp16, non-causal, N = 512 ... 8192; 10 warm-up calls,
+    50 timed), through rattn_fwd (which picks its kernel by itself).  Only
+    this library is timed: the page's own comparison is not reproduced."""
+    out = {}
+    for n in (512, 1024, 2048, 4096, 8192):
+        q, k, v = workloads.make_qkv(2, n, n, 32, 32, 128, torch.float16, seed=n, device=dev)
+
+        def run():
+            return binding.fwd(q, k, v)
+        warm_up(torch, run, 10)
+        ms = loop_ms(torch, run, 50)
+        flop = 4 * 128 * 32 * 2 * n * n
+        out[f"page_bench_b2_h32_n{n}_d128_f16"] = {
+            "ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "pct_of_peak": round(100 * flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        del q, k, v
+    return out
 
 
 def main():
@@ -659,6 +700,8 @@ def main():
             extras[we.name] = {"ms": round(ms, 4), "tflops": round(fe / (ms * 1e-3) / 1e12, 2),
                                "pct_of_peak": round(100 * fe / (ms * 1e-3) / 1e12
                                                     / PEAK_BF16_TFLOPS, 2)}
+            if idx == 2:  # latency-sized: the device time of one call as well
+                extras[we.name]["device_us"] = round(device_us(torch, run), 2)
             ns = binding.split_hint(qe, ke, we.W, we.zigzag, we.rank)
             if ns > 1:  # too few query tiles for the GPU: the split-KV entry point
                 ws = torch.empty(ns * qe.numel() // we.d * (we.d + 1), dtype=torch.float32,
@@ -681,6 +724,7 @@ def main():
         for idx in (2, 3):
             workload_extra(idx)
         extras.update(tiny_latency_extra(torch, binding, workloads, dev, args))
+        extras.update(page_benchmark_sweep(torch, binding, workloads, dev, args))
         extras.update(small_d_sweep(torch, binding, workloads, dev, args))
         extras.update(backward_extras(torch, binding, ring, workloads, dev, args))
         extras.update(layout_comparison(torch, binding, ring, workloads, dev, args))
@@ -851,9 +895,10 @@ def single_head_extra(torch, binding, workloads, dev, args):
         return binding.fwd(q, k, v)
     warm_up(torch, run, 5)
     ms = loop_ms(torch, run, max(50, 2 * args.steps))
+    dev_us = device_us(torch, run)
     groups = w.B * w.Hq * ((w.Nq + 31) // 32)
     kv_bytes = 2 * w.N * w.Hkv * w.d * 2
-    return {w.name: {"ms": round(ms, 4), "us": round(ms * 1e3, 2),
+    return {w.name: {"ms": round(ms, 4), "us": round(ms * 1e3, 2), "device_us": round(dev_us, 2),
                      "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
                      "pct_of_peak": round(100 * flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                      "kernel": "fwd_short_kernel (32 query rows per workgroup, key tiles split "
