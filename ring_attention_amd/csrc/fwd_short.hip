@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
 
   // ---- work item: 32 query rows of one (batch, head) -----------------------
   const int32_t BH = p.B * p.Hq;
-  const WorkItem wi = work_item_of(blockIdx.x, BH, 1);
+  const WorkItem wi = work_item_of(blockIdx.x, BH, p.n_splits);
   const int32_t bh = xcd_head_swizzle(wi.bh, BH);
   const int32_t b = bh / p.Hq, hq = bh % p.Hq, hkv = hq / p.group;
   const QTile qt = query_tile(s, wi.t_lin, kBr);
@@ -131,9 +131,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
     }
   }
 
-  // ---- this wave's key tiles: [T w / 8, T (w+1) / 8) of the T live tiles ---
-  const int64_t T = count_live_tiles<BC>(s, qt.rank, qhi);
-  const int64_t t0 = (T * wave) >> 3, t1 = (T * (wave + 1)) >> 3;
+  // ---- this wave's key tiles ------------------------------------------------
+  // split s of n takes live tiles [A s / n, A (s+1) / n) of the A live tiles
+  // (split-KV launches; n = 1 otherwise), and wave w of the workgroup takes
+  // [b0 + T w / 8, b0 + T (w+1) / 8) of those T tiles
+  const int64_t all = count_live_tiles<BC>(s, qt.rank, qhi);
+  int64_t b0 = 0, b1 = all;
+  if (p.n_splits > 1) {  // the 64-bit divisions run in software: only when split
+    b0 = all * wi.split / p.n_splits;
+    b1 = all * (wi.split + 1) / p.n_splits;
+  }
+  const int64_t T = b1 - b0;
+  const int64_t t0 = b0 + ((T * wave) >> 3), t1 = b0 + ((T * (wave + 1)) >> 3);
   const int n = (int)(t1 - t0);
   TileCursor cur = cursor_at<BC>(s, qt.rank, qhi, t0);
 
@@ -414,7 +423,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_short_kernel(
   const float lse_n = seen ? mx * kLn2 + logf(lsum) : kNegInf;
   const int64_t orow = ((int64_t)b * p.out_rows + p.out_row_off + qt.row0 + row) * p.Hq + hq;
   if constexpr (OUT_F32) {
-    float* out_f = (float*)out;
+    // split-KV: this split's plane of the partial results
+    float* out_f = (float*)out + wi.split * p.split_out_stride;
+    lse += wi.split * p.split_lse_stride;
     f32x4* dst = (f32x4*)(out_f + orow * D + c8);
     MergeW mw{0.f, 1.f, lse_n};
     f32x4 prev0 = f32x4{}, prev1 = f32x4{};
@@ -452,7 +463,7 @@ template <typename TT, int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, void* out, float* lse,
                     bool out_f32, const FwdParams& p, const Sched& s, hipStream_t stream) {
   using E = typename TT::elem;
-  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq;
+  const int64_t blocks = (int64_t)s.n_tiles * p.B * p.Hq * p.n_splits;
   if (blocks <= 0) return hipSuccess;
   const bool buf = (uint64_t)p.Nk * (uint64_t)p.Hkv * D * sizeof(E) <= 0xFFFF0000ull;
   const dim3 g((unsigned)blocks), t(kThreads);

@@ -126,10 +126,12 @@ bool retile(Sched& s, int br) {
 // 87 -> 69; 8 non-causal heads of 4096 stay on the 256-row kernel (93 against
 // 117); d = 64 fp16 one head 64 -> 20, (B, N, H) = (2, 1024, 4) 22 -> 13;
 // d = 32 one head 67 -> 15, 16 non-causal heads of 2048 39 -> 29.
+// Split-KV launches decide on the same unsplit items; each split of a query
+// tile is then one workgroup of the key-split kernel.
 // The environment variable RATTN_FWD_SHORT overrides the choice for every
 // eligible launch: "0" never takes the key-split kernel, "1" always does.
 bool short_launch(int dtype, int d, const FwdParams& p, const Sched& s) {
-  if (!use_mfma(dtype, d) || d < 32 || p.n_splits != 1 || s.mode == kVisitVarlen) return false;
+  if (!use_mfma(dtype, d) || d < 32 || s.mode == kVisitVarlen) return false;
   const char* env = getenv("RATTN_FWD_SHORT");
   if (env && env[0] == '0' && env[1] == 0) return false;
   if (env && env[0] == '1' && env[1] == 0) return true;
@@ -155,7 +157,7 @@ int dispatch(int dtype, int d, const void* q, const void* k, const void* v, void
   hipError_t e;
   if (short_launch(dtype, d, p, s)) {
     Sched s32 = s;
-    if (retile(s32, kShortBr) && (int64_t)s32.n_tiles * p.B * p.Hq <= INT32_MAX) {
+    if (retile(s32, kShortBr) && (int64_t)s32.n_tiles * p.B * p.Hq * p.n_splits <= INT32_MAX) {
       e = launch_fwd_short(dtype, d, q, k, v, out, lse, out_f32, p, s32, (hipStream_t)stream);
       return e == hipSuccess ? RATTN_OK : RATTN_EHIP;
     }
@@ -403,6 +405,20 @@ extern "C" int rattn_split_hint(int B, int Hq, int64_t Nq, int64_t N, int d, int
   if (check_dtype_d(dtype, d) != RATTN_OK) return 1;
   const int64_t br = tile_rows(dtype, d);
   const int64_t items = (Nq + br - 1) / br * B * Hq;
+  // Launches this small run on the key-split kernel (32 query rows per
+  // workgroup) unless RATTN_FWD_SHORT=0: aim at one of its workgroups per
+  // compute unit, each wave keeping at least 4 key tiles of 32 (one head of
+  // 4096 queries: 128 workgroups, 2 splits).
+  const char* env = getenv("RATTN_FWD_SHORT");
+  const bool short_off = env && env[0] == '0' && env[1] == 0;
+  if (!short_off && dtype != RATTN_F32 && d >= 32 && items * 4 <= (int64_t)n_cu) {
+    const int64_t groups = (Nq + kShortBr - 1) / kShortBr * B * Hq;
+    int64_t n = (int64_t)n_cu / groups;
+    const int64_t cap = ((N + 31) / 32) / (8 * 4);
+    if (n > cap) n = cap;
+    if (n > kMaxSplits) n = kMaxSplits;
+    return n < 1 ? 1 : (int)n;
+  }
   // Half as many workgroups as compute units already hides most of the
   // split's cost (partials written and merged); measured on 4096 x 4096,
   // one head: 8 splits (128 workgroups) beat 4, 16 and 32.

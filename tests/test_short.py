@@ -184,3 +184,48 @@ def test_queued_small_launch_matches_fwd(gpu):
     b_o, b_l = binding.fwd_queued(q, k, v, causal=True, queue_ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(a_o, b_o) and torch.equal(a_l, b_l)
+
+
+# split-KV on the key-split kernel: each split of a 32-row query tile is one
+# workgroup (its 8 waves divide the split's key tiles), partials in the
+# workspace, then the n-way log-sum-exp combine
+
+
+@pytest.mark.fwd_short("1")
+@pytest.mark.parametrize("d", [128, 64, 32])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_splits", [2, 3, 8])
+def test_split_kv(gpu, d, causal, n_splits):
+    q, k, v = workloads.make_qkv(2, 1000, 1000, 4, 2, d, torch.bfloat16, seed=d + n_splits)
+    tp.run_split_check(q, k, v, causal, 1, False, -1, n_splits,
+                       f"short split d={d} causal={causal} n={n_splits}")
+
+
+@pytest.mark.fwd_short("1")
+@pytest.mark.parametrize("W,zigzag,rank", [(4, True, 1), (4, True, -1), (3, False, 2)])
+def test_split_kv_ring_layouts(gpu, W, zigzag, rank):
+    N = 2 * W * 100 if zigzag else W * 160
+    q, k, v = workloads.make_qkv(1, N, N, 2, 1, 128, torch.float16, seed=W + rank)
+    if rank >= 0:
+        from ring_attention_amd import ring
+        q = ring.shard(q, W, zigzag, rank)
+    tp.run_split_check(q, k, v, True, W, zigzag, rank, 3,
+                       f"short split W={W} zigzag={zigzag} rank={rank}")
+
+
+@pytest.mark.fwd_short("auto")
+def test_split_kv_workload2_auto(gpu):
+    """Workload 2 with the split count the hint gives for the key-split
+    kernel (2 on a 256-CU GPU), against the oracle; the allocation-free entry
+    point gives the same bits."""
+    w = workloads.workload(2)
+    q, k, v = workloads.make_inputs(w)
+    ns = binding.split_hint(q.to(gpu), k.to(gpu))
+    tp.note(f"case {w.name}: key-split kernel with {ns} splits")
+    assert ns >= 1
+    tp.run_split_check(q, k, v, False, 1, False, -1, ns, w.name + f" short split {ns}")
+    qd, kd, vd = q.to(gpu), k.to(gpu), v.to(gpu)
+    a_o, a_l = binding.fwd_split(qd, kd, vd, n_splits=ns)
+    b_o, b_l = binding.fwd_split_noalloc(qd, kd, vd, n_splits=ns)
+    torch.cuda.synchronize()
+    assert torch.equal(a_o, b_o) and torch.equal(a_l, b_l)
