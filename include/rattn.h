@@ -89,6 +89,14 @@ typedef enum { RATTN_F32 = 0, RATTN_F16 = 1, RATTN_BF16 = 2 } rattn_dtype;
  * every call this kernel can serve).  The same choice applies to
  * rattn_fwd_queued and the ring-step calls; results agree within the stated
  * tolerances, not bit for bit, between the two kernels.
+ *
+ * Debugging: with RATTN_SERIALIZE=1 (read at every call) the 256-row kernel
+ * runs one key tile at a time, each tile requested and waited for right
+ * before it is used and a workgroup barrier around every phase, and the
+ * 32-row kernel is not chosen.  It computes the same arithmetic in the same
+ * order, so its results equal those of the pipelined schedule bit for bit;
+ * a difference points at an LDS buffering hazard.  It is slow: not for use
+ * beyond debugging.  rattn_fwd_queued then runs one workgroup per item.
  */
 RATTN_API int rattn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
               int B, int Hq, int Hkv, int64_t Nq, int64_t N, int d, int dtype,

@@ -42,6 +42,8 @@
 // the compiler adds no conservative waits between a DMA and unrelated LDS
 // reads.  The LDS address is an M0 operand of the asm, so the compiler
 // writes M0 itself and knows the asm reads it.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "kcommon.h"
@@ -192,7 +194,13 @@ __device__ __forceinline__ void run_next(RunCursor& c, const RunCursorCtx& x) {
 
 // One work item (a query tile of a (batch, head), or one key split of it):
 // work item `item` of the enumeration work_item_of describes.
-template <typename TT, int D, bool OUT_F32, bool BUF, bool QUEUED>
+// SERIAL: the debug form of the schedule (RATTN_SERIALIZE=1): one tile in
+// flight, requested and waited for by every wave right before the phase that
+// reads it, both wave groups in lockstep with a workgroup barrier around every
+// phase.  Every wave performs the same arithmetic in the same order as in the
+// pipelined schedule, so the two must agree bit for bit; a difference points
+// at an LDS buffering hazard of the pipelined one.
+template <typename TT, int D, bool OUT_F32, bool BUF, bool QUEUED, bool SERIAL = false>
 __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q,
                                          const typename TT::elem* __restrict__ k,
                                          const typename TT::elem* __restrict__ v,
@@ -400,9 +408,11 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
     uint4* z = (uint4*)(smem + (kNBuf - 1) * kBufBytes + kTileBytes);
     for (int i = tid; i < kTileBytes / 16; i += kThreads) z[i] = uint4{0, 0, 0, 0};
   }
-  issue_all(plan_next());  // tile 0
-  issue_all(plan_next());  // tile 1
-  if (T > 1) wait_dma_but_one_tile<kDmaPerWave>(); else wait_dma_all();
+  if constexpr (!SERIAL) {
+    issue_all(plan_next());  // tile 0
+    issue_all(plan_next());  // tile 1
+    if (T > 1) wait_dma_but_one_tile<kDmaPerWave>(); else wait_dma_all();
+  }
   __syncthreads();
 
   // per-group state carried between phases
@@ -593,7 +603,29 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
   // M_{m-3}, window m-2) finished at the barrier ending window m-2.  Tile m
   // is complete on every wave at the barrier ending window m, before any QK
   // of tile m (window m+1).  Both groups pass T+1 barriers.
-  if (group == 0) {
+  if constexpr (SERIAL) {
+    // phase kk: tile kk lands, then {PV of tile kk-1, QK of tile kk}, then
+    // the softmax of tile kk
+    for (int kk = 0; kk <= T; ++kk) {
+      if (kk < T) {
+        issue_all(plan_next());
+        wait_dma_all();
+      }
+      __syncthreads();
+      const char* pvb = smem + ((kk - 1) & (kNBuf - 1)) * kBufBytes;
+      const char* qkb = smem + (kk & (kNBuf - 1)) * kBufBytes;
+      if (kk == 0) {
+        if (T > 0) mfma_stream(no{}, yes{}, pvb, qkb);
+      } else if (kk < T) {
+        mfma_stream(yes{}, yes{}, pvb, qkb);
+      } else {
+        mfma_stream(yes{}, no{}, pvb, qkb);
+      }
+      __syncthreads();
+      if (kk < T) v_phase();
+      __syncthreads();
+    }
+  } else if (group == 0) {
     m_phase(0, no{}, yes{});
     slot_barrier();
     for (int j = 0; j + 1 < T; ++j) {
@@ -623,7 +655,9 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
   if (!q_valid) return;
   const bool seen = l_tot > 0.f;
   const float inv = seen ? 1.f / l_tot : 0.f;
-  const float lse_n = seen ? m_run * kLn2 + logf(l_tot) : kNegInf;
+  // explicit fused forms, so that every instantiation (the serialized one
+  // included) rounds the same way
+  const float lse_n = seen ? fmaf(m_run, kLn2, logf(l_tot)) : kNegInf;
   const int64_t orow = ((int64_t)b * p.out_rows + p.out_row_off + qt.row0 + my_q) * p.Hq + hq;
   float* out_f = (float*)out + wi.split * p.split_out_stride;
   float* lse_w = lse + wi.split * p.split_lse_stride;
@@ -652,7 +686,9 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * f_n;
         f32x4* dst = (f32x4*)(out_f + orow * D + d0);
-        if (merging) o4 += prev[4 * db + j] * mw.f_r;
+        if (merging)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = fmaf(prev[4 * db + j][e], mw.f_r, o4[e]);
         *dst = o4;
       } else {
         v4 o4;
@@ -672,6 +708,15 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_kernel
     const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
     FwdParams p, Sched s) {
   fwd_item<TT, D, OUT_F32, BUF, false>(q, k, v, out, lse, p, s, blockIdx.x);
+}
+
+// The serialized debug schedule of the same work items (RATTN_SERIALIZE=1).
+template <typename TT, int D, bool OUT_F32, bool BUF>
+__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 4) void fwd_mfma128_serial_kernel(
+    const typename TT::elem* __restrict__ q, const typename TT::elem* __restrict__ k,
+    const typename TT::elem* __restrict__ v, void* __restrict__ out, float* __restrict__ lse,
+    FwdParams p, Sched s) {
+  fwd_item<TT, D, OUT_F32, BUF, false, true>(q, k, v, out, lse, p, s, blockIdx.x);
 }
 
 // The same work items taken from queues instead of one workgroup each: a grid
@@ -761,6 +806,19 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* out, floa
   const bool buf = (uint64_t)p.Nk * (uint64_t)p.Hkv * D * sizeof(E) <= 0xFFFF0000ull;
   const dim3 g((unsigned)blocks), t(kThreads);
   const E *qe = (const E*)q, *ke = (const E*)k, *ve = (const E*)v;
+  // RATTN_SERIALIZE=1: the serialized debug schedule, one workgroup per item
+  const char* ser = getenv("RATTN_SERIALIZE");
+  if (ser && ser[0] == '1' && ser[1] == 0) {
+    if (out_f32 && buf)
+      hipLaunchKernelGGL((fwd_mfma128_serial_kernel<TT, D, true, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    else if (out_f32)
+      hipLaunchKernelGGL((fwd_mfma128_serial_kernel<TT, D, true, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    else if (buf)
+      hipLaunchKernelGGL((fwd_mfma128_serial_kernel<TT, D, false, true>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    else
+      hipLaunchKernelGGL((fwd_mfma128_serial_kernel<TT, D, false, false>), g, t, 0, stream, qe, ke, ve, out, lse, p, s);
+    return hipGetLastError();
+  }
   // queued launches at d = 128 only: at d = 64 and 32 the loop around the
   // item does not fit the register budget of two workgroups per compute unit
   if constexpr (D == 128) if (queues && blocks <= 0xFFFFFFF0ll) {

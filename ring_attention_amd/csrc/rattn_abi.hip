@@ -134,6 +134,8 @@ bool short_launch(int dtype, int d, const FwdParams& p, const Sched& s) {
   if (!use_mfma(dtype, d) || d < 32 || s.mode == kVisitVarlen) return false;
   const char* env = getenv("RATTN_FWD_SHORT");
   if (env && env[0] == '0' && env[1] == 0) return false;
+  const char* ser = getenv("RATTN_SERIALIZE");  // the 256-row kernel's debug schedule
+  if (ser && ser[0] == '1' && ser[1] == 0) return false;
   if (env && env[0] == '1' && env[1] == 0) return true;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
