@@ -652,6 +652,48 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
   }
   // ---- epilogue: O / l, LSE = m ln2 + ln l --------------------------------
   const float l_tot = pair_sum(l_run);
+  if constexpr (!OUT_F32) {
+    // 16-bit output: the normalised rows go through LDS, so that the global
+    // stores write whole rows, consecutive lanes along a row, instead of 8
+    // bytes in each of 32 rows per store instruction.  A staged row is 2D
+    // bytes plus 16 of padding (16-byte aligned; it spreads the rows of one
+    // fragment store over the banks).
+    constexpr int kStageRow = 2 * D + 16;
+    static_assert(kBr * kStageRow <= (kNBuf - 1) * kBufBytes + kTileBytes,
+                  "staging stays clear of the zeroed V block");
+    __syncthreads();  // both groups are done with the ring buffers
+    if (q_valid) {
+      const bool seen = l_tot > 0.f;
+      const float inv = seen ? 1.f / l_tot : 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = to_elem<TT>(oacc[db][4 * j + e] * inv);
+          *(v4*)(smem + my_q * kStageRow + 2 * (32 * db + 8 * j + 4 * hl)) = o4;
+        }
+      if (hl == 0) {
+        const int64_t orow = ((int64_t)b * p.out_rows + p.out_row_off + qt.row0 + my_q) * p.Hq + hq;
+        lse[wi.split * p.split_lse_stride + orow] = seen ? fmaf(m_run, kLn2, logf(l_tot)) : kNegInf;
+      }
+    }
+    __syncthreads();
+    constexpr int kChunks = 2 * D / 16;  // 16-byte chunks per row
+#pragma unroll 1
+    for (int i = 0; i < kBr * kChunks / kThreads; ++i) {
+      const int id = i * kThreads + tid;
+      const int r = id / kChunks, c = id % kChunks;
+      if (r < qt.rows) {
+        const int64_t grow = ((int64_t)b * p.out_rows + p.out_row_off + qt.row0 + r) * p.Hq + hq;
+        *(uint4*)((char*)out + grow * (2 * D) + 16 * c) = *(const uint4*)(smem + r * kStageRow + 16 * c);
+      }
+    }
+    return;
+  }
+  // float32 output (ring steps, split-KV partials): one 16-byte store per
+  // lane and fragment
   if (!q_valid) return;
   const bool seen = l_tot > 0.f;
   const float inv = seen ? 1.f / l_tot : 0.f;
@@ -681,21 +723,13 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d0 = 32 * db + 8 * j + 4 * hl;
-      if (OUT_F32) {
-        f32x4 o4;
+      f32x4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * f_n;
-        f32x4* dst = (f32x4*)(out_f + orow * D + d0);
-        if (merging)
+      for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * f_n;
+      if (merging)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = fmaf(prev[4 * db + j][e], mw.f_r, o4[e]);
-        *dst = o4;
-      } else {
-        v4 o4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = to_elem<TT>(oacc[db][4 * j + e] * inv);
-        *(v4*)((E*)out + orow * D + d0) = o4;
-      }
+        for (int e = 0; e < 4; ++e) o4[e] = fmaf(prev[4 * db + j][e], mw.f_r, o4[e]);
+      *(f32x4*)(out_f + orow * D + d0) = o4;
     }
   if (hl == 0) lse_w[orow] = mw.lse;
 }
