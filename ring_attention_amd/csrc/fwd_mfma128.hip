@@ -652,12 +652,14 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
   }
   // ---- epilogue: O / l, LSE = m ln2 + ln l --------------------------------
   const float l_tot = pair_sum(l_run);
-  if constexpr (!OUT_F32) {
-    // 16-bit output: the normalised rows go through LDS, so that the global
-    // stores write whole rows, consecutive lanes along a row, instead of 8
-    // bytes in each of 32 rows per store instruction.  A staged row is 2D
-    // bytes plus 16 of padding (16-byte aligned; it spreads the rows of one
-    // fragment store over the banks).
+  if constexpr (!OUT_F32 && !QUEUED) {
+    // 16-bit output, one workgroup per item: the normalised rows go through
+    // LDS, so that the global stores write whole rows, consecutive lanes
+    // along a row, instead of 8 bytes in each of 32 rows per store
+    // instruction.  A staged row is 2D bytes plus 16 of padding (16-byte
+    // aligned; it spreads the rows of one fragment store over the banks).
+    // The queued kernel keeps the direct stores: with staging its items
+    // read twice the bytes from HBM (the run time unchanged).
     constexpr int kStageRow = 2 * D + 16;
     static_assert(kBr * kStageRow <= (kNBuf - 1) * kBufBytes + kTileBytes,
                   "staging stays clear of the zeroed V block");
@@ -692,8 +694,8 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
     }
     return;
   }
-  // float32 output (ring steps, split-KV partials): one 16-byte store per
-  // lane and fragment
+  // float32 output (ring steps, split-KV partials) and the queued kernel's
+  // 16-bit output: each lane stores its own fragments
   if (!q_valid) return;
   const bool seen = l_tot > 0.f;
   const float inv = seen ? 1.f / l_tot : 0.f;
@@ -723,13 +725,21 @@ __device__ __forceinline__ void fwd_item(const typename TT::elem* __restrict__ q
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d0 = 32 * db + 8 * j + 4 * hl;
-      f32x4 o4;
+      if (OUT_F32) {
+        f32x4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * f_n;
-      if (merging)
+        for (int e = 0; e < 4; ++e) o4[e] = oacc[db][4 * j + e] * f_n;
+        f32x4* dst = (f32x4*)(out_f + orow * D + d0);
+        if (merging)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = fmaf(prev[4 * db + j][e], mw.f_r, o4[e]);
-      *(f32x4*)(out_f + orow * D + d0) = o4;
+          for (int e = 0; e < 4; ++e) o4[e] = fmaf(prev[4 * db + j][e], mw.f_r, o4[e]);
+        *dst = o4;
+      } else {
+        v4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = to_elem<TT>(oacc[db][4 * j + e] * inv);
+        *(v4*)((E*)out + orow * D + d0) = o4;
+      }
     }
   if (hl == 0) lse_w[orow] = mw.lse;
 }
